@@ -1,0 +1,218 @@
+"""ctypes binding of libmla_hip.so (argument marshalling only).
+
+Every function here checks tensor placement, dtype and contiguity, allocates
+missing outputs/workspace with torch on the query's device, and calls the C
+entry point of the same name on the current HIP stream.  All arithmetic runs
+in the HIP kernels; if the library is missing, loading fails loudly.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3 = 1
+LATENT_DIM = 576
+VALUE_DIM = 512
+
+_STATUS_NAMES = {
+    0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_SHAPE", 3: "MLA_ERR_BAD_DTYPE",
+    4: "MLA_ERR_BAD_SCALE", 5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_HIP",
+}
+
+# Every symbol include/mla.h declares.
+EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_verify", "mla_split",
+           "mla_merge", "mla_status_string", "mla_last_hip_error")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len_hint", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+
+
+def load(path=None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is missing; build it with "
+                           "`python -m decode_attention_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    pp = ctypes.POINTER(Params)
+    lib.mla_num_splits.argtypes = [pp]
+    lib.mla_num_splits.restype = i32
+    lib.mla_workspace_size.argtypes = [pp]
+    lib.mla_workspace_size.restype = sz
+    for name in ("mla_decode", "mla_verify"):
+        fn = getattr(lib, name)
+        fn.argtypes = [pp, vp, vp, vp, vp, f32, f32, vp, vp, vp, sz, vp]
+        fn.restype = i32
+    lib.mla_split.argtypes = [pp, vp, vp, vp, vp, f32, f32, vp, vp, vp]
+    lib.mla_split.restype = i32
+    lib.mla_merge.argtypes = [vp, vp, i32, ctypes.c_int64, vp, vp, vp]
+    lib.mla_merge.restype = i32
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_hip_error.argtypes = []
+    lib.mla_last_hip_error.restype = i32
+    _LIB = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        lib = load()
+        msg = lib.mla_status_string(status).decode()
+        if status == 7:
+            msg += f" (hipError {lib.mla_last_hip_error()})"
+        raise MLAError(status, msg)
+
+
+def _kv_dtype(kv_cache):
+    if kv_cache.dtype == torch.bfloat16:
+        return MLA_KV_BF16
+    if kv_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MLA_KV_FP8_E4M3
+    raise MLAError(3, f"kv_cache dtype {kv_cache.dtype} is neither bfloat16 nor FP8 E4M3FN bytes")
+
+
+def make_params(q, kv_cache, page_table, num_splits=0, max_seq_len_hint=0):
+    return Params(batch=q.shape[0], num_q_tokens=q.shape[1], num_heads=q.shape[2],
+                  num_blocks=kv_cache.shape[0], max_blocks_per_seq=page_table.shape[1],
+                  max_seq_len_hint=int(max_seq_len_hint), kv_dtype=_kv_dtype(kv_cache),
+                  num_splits=int(num_splits))
+
+
+def _check_inputs(q, kv_cache, page_table, seq_lens):
+    dev = q.device
+    if dev.type != "cuda":
+        raise MLAError(2, "q must be a GPU tensor")
+    for name, t in (("kv_cache", kv_cache), ("page_table", page_table), ("seq_lens", seq_lens)):
+        if t.device != dev:
+            raise MLAError(2, f"{name} is on {t.device}, q on {dev}")
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[3] != LATENT_DIM or not q.is_contiguous():
+        raise MLAError(2, "q must be contiguous bf16 [B, Q, H, 576]")
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (16, LATENT_DIM) or not kv_cache.is_contiguous():
+        raise MLAError(2, "kv_cache must be contiguous [num_blocks, 16, 576]")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous() \
+            or page_table.shape[0] != q.shape[0]:
+        raise MLAError(2, "page_table must be contiguous int32 [B, max_blocks_per_seq]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
+        raise MLAError(2, "seq_lens must be contiguous int32 [B]")
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def num_splits(q, kv_cache, page_table, num_splits=0, max_seq_len_hint=0):
+    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
+    return int(load().mla_num_splits(ctypes.byref(p)))
+
+
+def workspace_size(q, kv_cache, page_table, num_splits=0, max_seq_len_hint=0):
+    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
+    return int(load().mla_workspace_size(ctypes.byref(p)))
+
+
+def _attend(entry, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, num_splits,
+            max_seq_len_hint, out, lse, workspace):
+    lib = load()
+    _check_inputs(q, kv_cache, page_table, seq_lens)
+    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
+    B, Q, H, _ = q.shape
+    if out is None:
+        out = torch.empty((B, Q, H, VALUE_DIM), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
+    need = int(lib.mla_workspace_size(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(getattr(lib, entry)(ctypes.byref(p), q.data_ptr(), kv_cache.data_ptr(),
+                               page_table.data_ptr(), seq_lens.data_ptr(), float(softmax_scale),
+                               float(kv_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
+                               _stream(q.device)))
+    return out, lse
+
+
+def decode(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
+           max_seq_len_hint=0, out=None, lse=None, workspace=None):
+    """mla_decode: Q = 1.  Returns (out bf16 [B,1,H,512], lse fp32 [B,1,H])."""
+    return _attend("mla_decode", q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale,
+                   num_splits, max_seq_len_hint, out, lse, workspace)
+
+
+def verify(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
+           max_seq_len_hint=0, out=None, lse=None, workspace=None):
+    """mla_verify: Q query tokens with the causal rule.  Returns (out, lse)."""
+    return _attend("mla_verify", q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale,
+                   num_splits, max_seq_len_hint, out, lse, workspace)
+
+
+def split(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
+          max_seq_len_hint=0, part_out=None, part_lse=None):
+    """mla_split: returns (part_out fp32 [S,B,Q,H,512], part_lse fp32 [S,B,Q,H])."""
+    lib = load()
+    _check_inputs(q, kv_cache, page_table, seq_lens)
+    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
+    S = int(lib.mla_num_splits(ctypes.byref(p)))
+    if S < 1:
+        raise MLAError(2, "invalid parameters")
+    B, Q, H, _ = q.shape
+    if part_out is None:
+        part_out = torch.empty((S, B, Q, H, VALUE_DIM), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((S, B, Q, H), dtype=torch.float32, device=q.device)
+    if part_out.numel() < S * B * Q * H * VALUE_DIM or part_lse.numel() < S * B * Q * H:
+        raise MLAError(2, "part_out / part_lse too small")
+    _check(lib.mla_split(ctypes.byref(p), q.data_ptr(), kv_cache.data_ptr(), page_table.data_ptr(),
+                         seq_lens.data_ptr(), float(softmax_scale), float(kv_scale),
+                         part_out.data_ptr(), part_lse.data_ptr(), _stream(q.device)))
+    return part_out, part_lse
+
+
+def merge(part_out, part_lse, out=None, lse=None):
+    """mla_merge over axis 0: part_out fp32 [S, ..., 512], part_lse fp32 [S, ...]."""
+    lib = load()
+    S = part_out.shape[0]
+    lead = tuple(part_out.shape[1:-1])
+    if part_out.shape[-1] != VALUE_DIM or tuple(part_lse.shape) != (S,) + lead:
+        raise MLAError(2, "part_out must be [S, ..., 512] and part_lse [S, ...]")
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32 \
+            or not part_out.is_contiguous() or not part_lse.is_contiguous():
+        raise MLAError(2, "partials must be contiguous float32")
+    rows = 1
+    for d in lead:
+        rows *= int(d)
+    if out is None:
+        out = torch.empty(lead + (VALUE_DIM,), dtype=torch.bfloat16, device=part_out.device)
+    if lse is None:
+        lse = torch.empty(lead, dtype=torch.float32, device=part_out.device)
+    _check(lib.mla_merge(part_out.data_ptr(), part_lse.data_ptr(), S, rows, out.data_ptr(),
+                         lse.data_ptr(), _stream(part_out.device)))
+    return out, lse

@@ -1,0 +1,196 @@
+// C ABI of the MLA library: host validation, split planning, launches.
+// Declarations and the full contract are in include/mla.h.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla.h"
+#include "mla_common.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kTargetWorkgroups = 512;  // two workgroups per CU on 256 CUs
+constexpr int kMinPagesPerSplit = 4;    // one 64-position tile
+
+mla_status check_params(const mla_params* p, int max_q) {
+  if (!p) return MLA_ERR_NULL_ARG;
+  if (p->batch < 1 || p->batch > 65535) return MLA_ERR_BAD_SHAPE;
+  if (p->num_q_tokens < 1 || p->num_q_tokens > max_q) return MLA_ERR_BAD_SHAPE;
+  if (p->num_heads < 1) return MLA_ERR_BAD_SHAPE;
+  if (p->num_heads > mla::kMaxHeads) return MLA_ERR_UNSUPPORTED;
+  if (p->num_blocks < 1 || p->max_blocks_per_seq < 1) return MLA_ERR_BAD_SHAPE;
+  if (p->max_seq_len_hint < 0) return MLA_ERR_BAD_SHAPE;
+  if (p->num_splits < 0 || p->num_splits > mla::kMaxSplits) return MLA_ERR_BAD_SHAPE;
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_BAD_DTYPE;
+  return MLA_OK;
+}
+
+int32_t choose_splits(const mla_params* p) {
+  if (p->num_splits > 0) return p->num_splits;
+  int64_t max_len = p->max_seq_len_hint > 0 ? p->max_seq_len_hint
+                                            : (int64_t)p->max_blocks_per_seq * mla::kPage;
+  int64_t pages = (max_len + mla::kPage - 1) / mla::kPage;
+  int64_t s = (kTargetWorkgroups + p->batch - 1) / p->batch;
+  int64_t cap = pages / kMinPagesPerSplit;
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > mla::kMaxSplits) s = mla::kMaxSplits;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+size_t rows_of(const mla_params* p) {
+  return (size_t)p->batch * (size_t)p->num_q_tokens * (size_t)p->num_heads;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t partial_bytes(const mla_params* p, int32_t S) {
+  const size_t rows = rows_of(p) * (size_t)S;
+  return align256(rows * mla::kValue * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+mla_status check_scales(float softmax_scale, float kv_scale, int32_t kv_dtype) {
+  if (!isfinite(softmax_scale)) return MLA_ERR_BAD_SCALE;
+  if (kv_dtype == MLA_KV_FP8_E4M3 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_BAD_SCALE;
+  return MLA_OK;
+}
+
+mla::SplitArgs make_args(const mla_params* p, const void* q, const void* kv, const int32_t* pt,
+                         const int32_t* sl, float softmax_scale, float kv_scale, int32_t S) {
+  mla::SplitArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint8_t*)kv;
+  a.page_table = pt;
+  a.seq_lens = sl;
+  a.batch = p->batch;
+  a.num_q = p->num_q_tokens;
+  a.heads = p->num_heads;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_splits = S;
+  const float ks = p->kv_dtype == MLA_KV_FP8_E4M3 ? kv_scale : 1.0f;
+  a.score_scale_log2 = (float)((double)softmax_scale * (double)ks * 1.4426950408889634);
+  a.out_scale = ks;
+  return a;
+}
+
+mla_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  g_last_hip_error = (int32_t)e;
+  return MLA_ERR_HIP;
+}
+
+mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
+                  const int32_t* pt, const int32_t* sl, float softmax_scale, float kv_scale,
+                  void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  mla_status st = check_params(p, max_q);
+  if (st != MLA_OK) return st;
+  if (!q || !kv || !pt || !sl || !out || !lse) return MLA_ERR_NULL_ARG;
+  st = check_scales(softmax_scale, kv_scale, p->kv_dtype);
+  if (st != MLA_OK) return st;
+  const int32_t S = choose_splits(p);
+  hipStream_t s = (hipStream_t)stream;
+  mla::SplitArgs a = make_args(p, q, kv, pt, sl, softmax_scale, kv_scale, S);
+  if (S == 1) {
+    a.out = (uint16_t*)out;
+    a.lse = lse;
+    return hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, true, s));
+  }
+  const size_t need = partial_bytes(p, S);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  const size_t rows = rows_of(p) * (size_t)S;
+  a.part_out = (float*)ws;
+  a.part_lse = (float*)((char*)ws + align256(rows * mla::kValue * sizeof(float)));
+  st = hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, false, s));
+  if (st != MLA_OK) return st;
+  mla::MergeArgs m{};
+  m.part_out = a.part_out;
+  m.part_lse = a.part_lse;
+  m.out = (uint16_t*)out;
+  m.lse = lse;
+  m.rows = (int64_t)rows_of(p);
+  m.num_splits = S;
+  return hip_status(mla::launch_merge(m, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_num_splits(const mla_params* p) {
+  if (check_params(p, mla::kMaxQ) != MLA_OK) return 0;
+  return choose_splits(p);
+}
+
+size_t mla_workspace_size(const mla_params* p) {
+  if (check_params(p, mla::kMaxQ) != MLA_OK) return 0;
+  const int32_t S = choose_splits(p);
+  return S == 1 ? 0 : partial_bytes(p, S);
+}
+
+mla_status mla_decode(const mla_params* p, const void* q, const void* kv_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, float softmax_scale,
+                      float kv_scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return attend(p, 1, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, out, lse,
+                workspace, workspace_bytes, stream);
+}
+
+mla_status mla_verify(const mla_params* p, const void* q, const void* kv_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, float softmax_scale,
+                      float kv_scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return attend(p, mla::kMaxQ, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, out,
+                lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
+                     const int32_t* page_table, const int32_t* seq_lens, float softmax_scale,
+                     float kv_scale, float* part_out, float* part_lse, void* stream) {
+  mla_status st = check_params(p, mla::kMaxQ);
+  if (st != MLA_OK) return st;
+  if (!q || !kv_cache || !page_table || !seq_lens || !part_out || !part_lse) return MLA_ERR_NULL_ARG;
+  st = check_scales(softmax_scale, kv_scale, p->kv_dtype);
+  if (st != MLA_OK) return st;
+  const int32_t S = choose_splits(p);
+  mla::SplitArgs a = make_args(p, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, S);
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  return hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, false, (hipStream_t)stream));
+}
+
+mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_splits, int64_t rows,
+                     void* out, float* lse, void* stream) {
+  if (!part_out || !part_lse || !out || !lse) return MLA_ERR_NULL_ARG;
+  if (num_splits < 1 || num_splits > 4096) return MLA_ERR_BAD_SHAPE;
+  if (rows < 1 || rows > ((int64_t)1 << 30)) return MLA_ERR_BAD_SHAPE;
+  mla::MergeArgs m{};
+  m.part_out = part_out;
+  m.part_lse = part_lse;
+  m.out = (uint16_t*)out;
+  m.lse = lse;
+  m.rows = rows;
+  m.num_splits = num_splits;
+  return hip_status(mla::launch_merge(m, (hipStream_t)stream));
+}
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "a size is out of range";
+    case MLA_ERR_BAD_DTYPE: return "unknown kv_dtype";
+    case MLA_ERR_BAD_SCALE: return "softmax_scale not finite, or kv_scale not finite and positive";
+    case MLA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case MLA_ERR_WORKSPACE: return "workspace missing or smaller than mla_workspace_size()";
+    case MLA_ERR_HIP: return "HIP runtime error (see mla_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int32_t mla_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

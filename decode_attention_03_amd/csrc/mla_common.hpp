@@ -1,0 +1,61 @@
+// Shared definitions of the gfx950 MLA kernels (device side) and their host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Geometry fixed by the method: one 576-wide latent per cached position
+// (512 latent + 64 rope dims), value vector = first 512 dims, pages of 16
+// positions ("Inside Kimi K3 optimization", section "1. Cache -- DCP";
+// "Kimi K2.6 + DFlash on 8x MI300X", section "Technical numbers").
+constexpr int kLatent = 576;
+constexpr int kValue = 512;
+constexpr int kPage = 16;
+
+// Workgroup shape of the split kernel: four wave64s, one KV page per wave per
+// tile, so a tile is 4 pages = 64 positions.
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTilePages = kWaves;
+constexpr int kTilePos = kTilePages * kPage;
+
+// Largest query-token count per launch and largest head count per token.
+constexpr int kMaxQ = 3;
+constexpr int kMaxHeads = 16;
+constexpr int kMaxSplits = 256;
+
+struct SplitArgs {
+  const uint16_t* q;          // bf16 [B][Q][H][576]
+  const uint8_t* kv;          // bf16 or fp8 [NB][16][576]
+  const int32_t* page_table;  // [B][max_blocks]
+  const int32_t* seq_lens;    // [B]
+  float* part_out;            // fp32 [S][B][Q][H][512]  (partial mode)
+  float* part_lse;            // fp32 [S][B][Q][H]
+  uint16_t* out;              // bf16 [B][Q][H][512]     (final mode, S == 1)
+  float* lse;                 // fp32 [B][Q][H]
+  int32_t batch;
+  int32_t num_q;
+  int32_t heads;
+  int32_t max_blocks;
+  int32_t num_splits;
+  float score_scale_log2;     // softmax_scale * kv_scale * log2(e)
+  float out_scale;            // kv_scale (value vectors are used undecoded-scale in the MFMA)
+};
+
+struct MergeArgs {
+  const float* part_out;      // [S][rows][512]
+  const float* part_lse;      // [S][rows]
+  uint16_t* out;              // bf16 [rows][512]
+  float* lse;                 // [rows]
+  int64_t rows;
+  int32_t num_splits;
+};
+
+// Host launchers (defined next to their kernels).  Return hipSuccess or the
+// launch error.
+hipError_t launch_split(const SplitArgs& a, bool fp8, bool final_out, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace mla

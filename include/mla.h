@@ -1,0 +1,158 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA decode / speculative-verify library.
+ *
+ * What is computed
+ * ----------------
+ * Multi-head Latent Attention over a paged, compressed KV cache.  Every cached
+ * position is one 576-wide latent (512 latent + 64 rope dims) shared by all
+ * query heads of the rank ("Inside Kimi K3 optimization", section
+ * "1. Cache -- DCP": 576 FP8 bytes per position; tensor parallelism splits
+ * heads, not the cache).  Each head dots its 576-wide query with the latent;
+ * the value vector is the first 512 dims of the same latent.  For sequence b,
+ * query token j (of Q) and head h:
+ *
+ *     s_t   = softmax_scale * kv_scale * <q[b,j,h,:], latent_t>     (t visible)
+ *     lse   = ln sum_t exp(s_t)
+ *     out[c] = sum_t exp(s_t - lse) * kv_scale * latent_t[c],   c < 512
+ *
+ * where latent_t is the stored value (bf16, or the decoded FP8 E4M3FN code),
+ * and kv_scale is the per-tensor FP8 scale (1 for bf16).
+ *
+ * Causal rule for speculative verify ("Inside Kimi K3 optimization",
+ * section "1. Cache -- DCP": multi-token verify): seq_lens[b] counts every
+ * cached position including the Q new tokens, and token j sees positions
+ * 0 .. seq_lens[b] - Q + j.  Q = 1 is plain decode.
+ *
+ * Split-KV ("Inside Kimi K3 optimization", section "4. MLA": the history is
+ * divided into pieces processed by parallel workgroups and the pieces are
+ * combined): sequence b has P_b = ceil(seq_lens[b] / 16) pages; split s of S
+ * covers pages [floor(s * P_b / S), floor((s + 1) * P_b / S)).  Each split
+ * produces a partial output normalised by its own softmax sum and its
+ * natural-log log-sum-exp (the "normalisation information" partial answers
+ * carry, section "1. Cache -- DCP"); mla_merge combines them.  A split with
+ * no visible position has lse = -inf and output 0.
+ *
+ * Head padding ("Inside Kimi K3 optimization", section "4. MLA"; "Kimi K3 on
+ * AMD MI355X", section "What had to be fixed"): heads are padded to 16 rows
+ * per query token inside the kernel with zero queries; pad rows are never
+ * read from or written to caller memory.
+ *
+ * Layouts (all row-major, contiguous, caller-owned device memory)
+ * --------------------------------------------------------------
+ *   q          bf16  [batch][num_q_tokens][num_heads][576]
+ *   kv_cache   bf16 or uint8 (FP8 E4M3FN codes) [num_blocks][16][576]
+ *              (block size 16: "Kimi K2.6 + DFlash on 8x MI300X",
+ *              section "Technical numbers")
+ *   page_table int32 [batch][max_blocks_per_seq]; entry p of row b is the
+ *              pool block holding positions 16p .. 16p+15 of sequence b; only
+ *              entries p < ceil(seq_lens[b] / 16) are read
+ *   seq_lens   int32 [batch]
+ *   out        bf16  [batch][num_q_tokens][num_heads][512]
+ *   lse        fp32  [batch][num_q_tokens][num_heads]   (natural log)
+ *   part_out   fp32  [S][batch][num_q_tokens][num_heads][512]
+ *   part_lse   fp32  [S][batch][num_q_tokens][num_heads]
+ *
+ * Conventions
+ * -----------
+ * - Every call is asynchronous on `stream` (a hipStream_t, NULL = default
+ *   stream); the library never allocates, frees or synchronises, and keeps no
+ *   state besides a per-thread last HIP error code.
+ * - Host-side validation runs before any HIP call; a failing call returns a
+ *   status and launches nothing.  After a launch, a HIP error maps to
+ *   MLA_ERR_HIP (the code is kept by mla_last_hip_error()).
+ * - Caller contract, not checked on the device: num_q_tokens <= seq_lens[b]
+ *   <= 16 * max_blocks_per_seq and 0 <= page_table[b][p] < num_blocks for the
+ *   pages read.  kv_cache and page_table are only read.
+ * - Concurrent calls on different streams are safe when their outputs and
+ *   workspaces do not overlap.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+  MLA_ERR_BAD_SHAPE = 2,    /* a size is out of range */
+  MLA_ERR_BAD_DTYPE = 3,    /* kv_dtype is not an mla_kv_dtype */
+  MLA_ERR_BAD_SCALE = 4,    /* softmax_scale not finite, or kv_scale not finite and > 0 */
+  MLA_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  MLA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than mla_workspace_size() */
+  MLA_ERR_HIP = 7           /* the HIP runtime reported an error */
+} mla_status;
+
+typedef enum {
+  MLA_KV_BF16 = 0,          /* bf16 latents, 1152 bytes per position */
+  MLA_KV_FP8_E4M3 = 1       /* OCP FP8 E4M3FN codes, 576 bytes per position, per-tensor kv_scale */
+} mla_kv_dtype;
+
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_q_tokens;       /* Q: 1 for mla_decode; 1..3 for mla_verify */
+  int32_t num_heads;          /* H: 1..16 (12 per TP8 rank); padded to 16 rows per token */
+  int32_t num_blocks;         /* pool blocks in kv_cache, >= 1 */
+  int32_t max_blocks_per_seq; /* page_table row stride, >= 1 */
+  int32_t max_seq_len_hint;   /* largest seq_len the caller expects; 0 = 16 * max_blocks_per_seq.
+                                 Only steers the automatic split count. */
+  int32_t kv_dtype;           /* mla_kv_dtype */
+  int32_t num_splits;         /* 0 = library chooses; 1..256 = exactly this many splits */
+} mla_params;
+
+/* Split count the library uses for these parameters (>= 1), or 0 if the
+ * parameters are invalid.  Depends only on host-side values. */
+int32_t mla_num_splits(const mla_params* p);
+
+/* Bytes of workspace mla_decode / mla_verify need: the partials of all splits
+ * (0 when the split count is 1).  Returns 0 for invalid parameters. */
+size_t mla_workspace_size(const mla_params* p);
+
+/* Single-token decode (p->num_q_tokens must be 1).  Writes out and lse.
+ * workspace: device memory of at least mla_workspace_size(p) bytes (may be
+ * NULL when that is 0); its contents are scratch. */
+mla_status mla_decode(const mla_params* p, const void* q, const void* kv_cache,
+                      const int32_t* page_table, const int32_t* seq_lens,
+                      float softmax_scale, float kv_scale, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Speculative verify: Q query tokens per sequence with the causal rule above
+ * (Q = 1 is allowed and equals mla_decode). */
+mla_status mla_verify(const mla_params* p, const void* q, const void* kv_cache,
+                      const int32_t* page_table, const int32_t* seq_lens,
+                      float softmax_scale, float kv_scale, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split-KV partials only: S = mla_num_splits(p) partial outputs (fp32,
+ * normalised by their own sums, already multiplied by kv_scale) and their
+ * natural-log normalisers, in the part_out / part_lse layouts above. */
+mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
+                     const int32_t* page_table, const int32_t* seq_lens,
+                     float softmax_scale, float kv_scale, float* part_out, float* part_lse,
+                     void* stream);
+
+/* Log-sum-exp merge of S partials ("normalisation information" lets shards be
+ * weighted correctly, "Inside Kimi K3 optimization", section "1. Cache -- DCP"):
+ *     lse[r] = ln sum_s exp(part_lse[s][r])        (-inf partials weigh 0)
+ *     out[r][c] = bf16_rne( sum_s exp(part_lse[s][r] - lse[r]) * part_out[s][r][c] )
+ * part_out fp32 [num_splits][rows][512], part_lse fp32 [num_splits][rows],
+ * out bf16 [rows][512], lse fp32 [rows].  All partials -inf: out 0, lse -inf.
+ * 1 <= num_splits <= 4096, rows >= 1. */
+mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_splits,
+                     int64_t rows, void* out, float* lse, void* stream);
+
+/* Static description of a status code. */
+const char* mla_status_string(int32_t status);
+
+/* HIP error code (hipError_t value) behind the last MLA_ERR_HIP on this thread. */
+int32_t mla_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

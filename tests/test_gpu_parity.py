@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the
+same seeded inputs, at the tolerance stated in parity_util.
+
+Small cases span several 64-position tiles with ragged tails, empty splits,
+1-3 query tokens, bf16 and FP8 KV, padded and unpadded head counts; the
+named workloads run at their full sizes in the launch configuration the
+bench uses, with the oracle evaluated on all sequences or a seeded sample.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import make_inputs, make_config, make_c5_layer
+from parity_util import (compare, oracle_out, oracle_partials, run_verify, split_page_ranges)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+SMALL_CASES = [
+    # (seq_lens, Q, H, kv_dtype, num_splits)
+    ([256], 1, 12, "bf16", 1),
+    ([1, 15, 16, 17, 64, 65, 200], 1, 12, "bf16", 0),
+    ([3, 63, 64, 65, 129, 300], 3, 12, "bf16", 0),
+    ([3, 63, 64, 65, 129, 300], 3, 12, "fp8", 0),
+    ([100, 1000], 2, 12, "fp8", 3),
+    ([517, 33], 3, 16, "bf16", 7),
+    ([517, 33], 1, 5, "fp8", 2),
+    ([2000], 3, 12, "fp8", 16),
+    ([4, 5, 6], 3, 12, "bf16", 1),
+    ([777], 2, 1, "bf16", 5),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[f"{c[3]}-Q{c[1]}-H{c[2]}-S{c[4]}-{len(c[0])}seq"
+                                                    for c in SMALL_CASES])
+def test_small_cases(gpu_lib, case):
+    lens, nq, nh, dt, S = case
+    _say(f"small case {case}")
+    inp = make_inputs(lens, nq, nh, dt, seed=sum(lens) + nq, device="cuda", spare_blocks=2,
+                      poison=True)
+    out, lse = run_verify(gpu_lib, inp, num_splits=S)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, str(case))
+
+
+def test_decode_entry_point(gpu_lib):
+    inp = make_inputs([50, 900, 2049], 1, 12, "fp8", seed=5, device="cuda")
+    out, lse = gpu_lib.decode(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
+                              inp.kv_scale)
+    torch.cuda.synchronize()
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, "decode")
+
+
+def test_c1_tiny(gpu_lib):
+    _say("config c1")
+    inp = make_config("c1", device="cuda")
+    for S in (0, 1, 2, 4):
+        out, lse = run_verify(gpu_lib, inp, num_splits=S)
+        ro, rl, _ = oracle_out(inp)
+        compare(out, lse, ro, rl, f"c1 S={S}")
+
+
+def test_c2_batched_decode(gpu_lib):
+    _say("config c2")
+    inp = make_config("c2", device="cuda")
+    out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=8192)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, "c2")
+
+
+def test_c3_spec_verify(gpu_lib):
+    _say("config c3")
+    inp = make_config("c3", device="cuda")
+    out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=32768)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, "c3")
+
+
+def test_c4_fp8_verify_sampled(gpu_lib):
+    _say("config c4")
+    inp = make_config("c4", device="cuda")
+    out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=65536)
+    idx = sorted(np.random.default_rng(404).choice(inp.batch, size=8, replace=False).tolist())
+    lens = inp.seq_lens.cpu().numpy()
+    idx = sorted(set(idx) | {int(np.argmax(lens)), int(np.argmin(lens))})
+    ro, rl, _ = oracle_out(inp, idx)
+    compare(out[idx], lse[idx], ro, rl, f"c4 seqs {idx}")
+
+
+@pytest.mark.parametrize("layer", [0, 23])
+def test_c5_long_context_layer(gpu_lib, layer):
+    _say(f"config c5 layer {layer}")
+    inp = make_c5_layer(layer, device="cuda")
+    S = 64
+    out, lse = run_verify(gpu_lib, inp, num_splits=S)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, f"c5 layer {layer}")
+
+
+def test_split_partials_match_oracle(gpu_lib):
+    """mla_split partials (each split's own normalised output and lse) against the
+    oracle's partials over the same page ranges, including empty splits."""
+    lens = [1, 40, 64, 300, 1000]
+    inp = make_inputs(lens, 3, 12, "fp8", seed=77, device="cuda")
+    S = 9
+    po, pl = gpu_lib.split(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
+                           inp.kv_scale, num_splits=S)
+    torch.cuda.synchronize()
+    ro, rl = oracle_partials(inp, S)
+    for s in range(S):
+        for b in range(len(lens)):
+            lo, hi = split_page_ranges(lens[b], S)[s]
+            if not np.isfinite(rl[s, b]).any():
+                assert torch.isneginf(pl[s, b]).all() and (po[s, b] == 0).all()
+                continue
+            fin = np.isfinite(rl[s, b])
+            got_l = pl[s, b].cpu().numpy()
+            assert np.array_equal(np.isfinite(got_l), fin)
+            assert np.abs(got_l[fin] - rl[s, b][fin]).max() <= 1e-3
+            got_o = po[s, b].cpu().numpy()
+            assert np.abs(got_o - ro[s, b]).max() <= 1e-2 * np.abs(ro[s, b]).max() + 1e-30
+
+
+def test_merge_matches_oracle(gpu_lib):
+    rng = np.random.default_rng(3)
+    S, rows = 13, 300
+    po = rng.normal(size=(S, rows, 512)).astype(np.float32)
+    pl = (rng.normal(size=(S, rows)) * 3).astype(np.float32)
+    pl[rng.random(size=(S, rows)) < 0.2] = -np.inf
+    pl[:, 7] = -np.inf          # a row with every partial empty
+    po[np.isneginf(pl)] = 0.0
+    out, lse = gpu_lib.merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64))
+    fin = np.isfinite(rl)
+    assert np.isneginf(lse.cpu().numpy()[~fin]).all()
+    assert (out.float().cpu().numpy()[~fin] == 0).all()
+    compare(out[fin], lse[fin], ro[fin], rl[fin], "merge")
+
+
+def test_deterministic_and_inputs_untouched(gpu_lib):
+    inp = make_inputs([300, 1234, 17], 3, 12, "fp8", seed=9, device="cuda")
+    kv0, pt0, q0 = inp.kv.clone(), inp.page_table.clone(), inp.q.clone()
+    o1, l1 = run_verify(gpu_lib, inp, num_splits=5)
+    o2, l2 = run_verify(gpu_lib, inp, num_splits=5)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(inp.kv, kv0) and torch.equal(inp.page_table, pt0) and torch.equal(inp.q, q0)
+
+
+def test_page_table_permutation_bitwise(gpu_lib):
+    """Same latents at permuted pool blocks (with poisoned spares and tails):
+    bitwise-equal outputs."""
+    lens = [70, 333, 1000]
+    a = make_inputs(lens, 3, 12, "bf16", seed=10, device="cuda", identity_pages=True)
+    nb = a.kv.shape[0]
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(nb + 5)).cuda()
+    pool = torch.full((nb + 5, 16, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pool[perm[:nb]] = a.kv
+    pt = torch.where(a.page_table >= 0, perm[a.page_table.clamp(min=0).long()].int(),
+                     a.page_table)
+    for b, L in enumerate(lens):
+        p = -(-L // 16)
+        pool[pt[b, p - 1].long(), L - (p - 1) * 16:] = float("nan")
+    oa, la = run_verify(gpu_lib, a, num_splits=4)
+    ob, lb = gpu_lib.verify(a.q, pool, pt.contiguous(), a.seq_lens, a.softmax_scale, 1.0,
+                            num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+
+
+def test_head_padding_bitwise(gpu_lib):
+    """12 heads vs the same 12 + 4 zero-query heads: the real heads are bitwise equal."""
+    inp = make_inputs([100, 900], 3, 12, "fp8", seed=11, device="cuda")
+    o12, l12 = run_verify(gpu_lib, inp, num_splits=3)
+    q16 = torch.zeros((2, 3, 16, 576), dtype=torch.bfloat16, device="cuda")
+    q16[:, :, :12] = inp.q
+    o16, l16 = gpu_lib.verify(q16, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
+                              inp.kv_scale, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(o16[:, :, :12], o12) and torch.equal(l16[:, :, :12], l12)
+
+
+def test_verify_equals_truncated_decodes(gpu_lib):
+    """Speculative verify is lossless: token j of a Q = 3 verify equals a decode
+    over the first L - 3 + j + 1 positions (within tolerance of the oracle)."""
+    lens = [200, 1500]
+    inp = make_inputs(lens, 3, 12, "fp8", seed=12, device="cuda")
+    ov, lv = run_verify(gpu_lib, inp)
+    for j in range(3):
+        sl = (inp.seq_lens - 3 + j + 1).int().contiguous()
+        od, ld = gpu_lib.decode(inp.q[:, j:j + 1].contiguous(), inp.kv, inp.page_table, sl,
+                                inp.softmax_scale, inp.kv_scale)
+        torch.cuda.synchronize()
+        ref = ov[:, j:j + 1].float().cpu().numpy().astype(np.float64)
+        compare(od, ld, ref, lv[:, j:j + 1].cpu().numpy().astype(np.float64), f"token {j}")
+
+
+def test_split_count_invariance(gpu_lib):
+    inp = make_inputs([1500, 64, 4097], 3, 12, "bf16", seed=13, device="cuda")
+    ro, rl, _ = oracle_out(inp)
+    for S in (1, 2, 8, 31, 64):
+        out, lse = run_verify(gpu_lib, inp, num_splits=S)
+        compare(out, lse, ro, rl, f"S={S}")
+
+
+def test_fp8_scale_not_rounded_into_operand(gpu_lib):
+    """kv_scale must stay out of the bf16 operand: with a scale whose products with
+    E4M3 values are not bf16-representable, the result still matches the oracle,
+    which uses decode(byte) * kv_scale exactly."""
+    inp = make_inputs([333], 3, 12, "fp8", seed=14, device="cuda")
+    inp.kv_scale = float(np.float32(0.0370000008))
+    out, lse = run_verify(gpu_lib, inp)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, "odd kv_scale")
+
+
+def test_errors_raise(gpu_lib):
+    inp = make_inputs([100], 1, 12, "bf16", seed=15, device="cuda")
+    with pytest.raises(gpu_lib.MLAError):
+        gpu_lib.verify(inp.q, inp.kv, inp.page_table, inp.seq_lens, float("nan"), 1.0)
+    q3 = torch.zeros((1, 3, 12, 576), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gpu_lib.MLAError):
+        gpu_lib.decode(q3, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale, 1.0)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gpu_lib.MLAError):
+        gpu_lib.verify(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale, 1.0,
+                       num_splits=4, workspace=ws)
