@@ -1,42 +1,51 @@
 // Split-KV MLA decode / verify kernel for gfx950 (MI355X).
 //
-// One workgroup = (split s, sequence b).  It walks its page range in tiles of
-// 4 pages (64 positions):
+// One workgroup (4 wave64s, one per SIMD) = (split s, sequence b).  It walks
+// its page range in tiles of 4 pages (64 positions):
 //
-//   a2  paged gather: each wave loads one 16-position page (contiguous in HBM)
-//       with 16-byte coalesced loads into registers, one tile ahead, and
-//       writes it to LDS as bf16 rows (positions past seq_len or past the
-//       split's pages are written as zeros, so nothing outside the visible
-//       history can reach an MFMA);
-//   a3  FP8 E4M3FN -> bf16 on that LDS write (v_cvt_scalef32_pk_bf16_fp8 with
-//       scale 1: exact); the per-tensor kv_scale is applied later in fp32, to
-//       the scores and to the output, never to the bf16 operand ("Inside Kimi
-//       K3 optimization", technical note on KDA precision: FP32 accumulation
-//       cannot recover inputs rounded earlier);
-//   a4  QK^T on MFMA (v_mfma_f32_16x16x32_bf16): wave w computes the scores
-//       of its page against every query row.  Rows are query tokens x heads,
-//       each token's heads padded to 16 rows with zero queries ("Inside Kimi
-//       K3 optimization", section "4. MLA"); the query stays in registers for
-//       the whole workgroup;
+//   a2  paged gather: each wave copies one 16-position page (contiguous in
+//       HBM) straight into LDS with 16-byte buffer_load_dwordx4 ... lds (no
+//       register staging), NBUF - 1 tiles ahead of the tile being computed
+//       (three buffers for FP8, two for bf16).  16-byte chunks are XOR-swizzled
+//       inside each latent row to spread LDS banks.  Positions past seq_len
+//       and pages past the split's range are zeroed in LDS, so nothing outside
+//       the visible history can reach an MFMA;
+//   a3  FP8 E4M3FN stays FP8 in LDS and is decoded exactly to bf16 right after
+//       each LDS read (v_cvt_scalef32_pk_bf16_fp8 with scale 1); the
+//       per-tensor kv_scale is applied in fp32 to the scores and to the
+//       output, never to the bf16 operand ("Inside Kimi K3 optimization",
+//       technical note on KDA precision: FP32 accumulation cannot recover
+//       inputs rounded earlier);
+//   a4  QK^T on MFMA.  Query rows are (token j, head h) packed as r = j*H + h.
+//       With more than 16 rows (speculative verify), rows 0..31 form a 32-row
+//       tile computed with v_mfma_f32_32x32x16_bf16 and rows 32..47 a 16-row
+//       tile computed with v_mfma_f32_16x16x32_bf16: 36 real rows cost 48
+//       padded rows, the 32x32 shape running ~1.6x more flops per cycle than
+//       16x16.  Zero query rows stand in for the padding ("Inside Kimi K3
+//       optimization", section "4. MLA").  Waves 0/1 own the 32-row tile over
+//       the two 32-position halves of the tile, waves 2/3 the 16-row tile; the
+//       query fragments stay in registers for the whole workgroup.  With at
+//       most 16 rows (decode), every wave owns one page against one 16-row tile;
 //   a5  causal mask + online softmax in the log2 domain; row maxima and row
-//       sums are reduced across lanes with shuffles and across the four waves
-//       through LDS;
-//   a6  PV on MFMA: the probabilities (bf16) go through LDS and each wave
-//       owns 128 of the 512 value columns; the value operand is the same LDS
-//       tile read transposed with ds_read_b64_tr_b16, so every KV byte is read
-//       from HBM once and serves both products;
-//   a7  epilogue: per-split output normalised by its own sum and its
-//       natural-log lse (partial mode), or bf16 out + lse directly when the
-//       launch has a single split.
+//       sums are reduced across lanes with shuffles and across waves in LDS;
+//   a6  PV on MFMA: probabilities (bf16) go through LDS; each wave owns 128 of
+//       the 512 value columns for every row; the value operand is the same LDS
+//       tile read transposed (ds_read_b64_tr_b8 for FP8, ds_read_b64_tr_b16
+//       for bf16), so every KV byte crosses HBM once and serves both products;
+//   a7  epilogue: per-split output normalised by its own sum plus its
+//       natural-log lse (partial mode), or bf16 out + lse when the launch has a
+//       single split.
 //
-// MFMA 16x16x32 bf16 lane layout (lane l, g = l / 16):
-//   A[m][k]: m = l % 16, k = 8g .. 8g+7;   B[k][n]: n = l % 16, k = 8g .. 8g+7;
-//   D[m][n]: n = l % 16, m = 4g .. 4g+3.
-// Scores are computed transposed, S^T[t][r] = K[t][:] . Q[r][:], so that a
-// lane owns one query row r = l % 16 of four positions t = 4g + i.  The output
-// is accumulated transposed as well, O^T[c][r] += V^T[c][t] P^T[t][r], so a
-// lane owns one row and four consecutive value columns.
+// MFMA lane layouts (lane l):
+//   16x16x32: A[m][k] m = l%16, k = 8(l/16)+j;  B[k][n] n = l%16, same k;
+//             D[m][n] n = l%16, m = 4(l/16)+i.
+//   32x32x16: A[m][k] m = l%32, k = 8(l/32)+j;  B[k][n] n = l%32, same k;
+//             D[m][n] n = l%32, m = 8(i/4) + 4(l/32) + i%4, i = 0..15.
+// Scores are computed transposed, S^T = K Q^T (a lane owns one query row), and
+// so is the output, O^T += V^T P^T (a lane owns one row and 4-column runs).
 #include <math.h>
+
+#include <type_traits>
 
 #include "mla_common.hpp"
 
@@ -47,302 +56,936 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kRowB = kLatent * 2 + 16;   // LDS bytes per bf16 latent row (+16 B skew)
-constexpr int kPRowB = kTilePos * 2 + 16; // LDS bytes per probability row
-constexpr int kKSteps = kLatent / 32;     // 18 MFMA k-steps over the 576 dims
-constexpr int kColTiles = kValue / kWaves / 16;  // 8 tiles of 16 value columns per wave
+constexpr int kLayout16 = 0;   // at most 16 query rows: one 16-row tile
+constexpr int kLayout48 = 1;   // 17..48 query rows: a 32-row tile + a 16-row tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
 
-__device__ __forceinline__ float wave_max16(float x) {
-  // max over lanes l, l^16, l^32, l^48 (the four position groups of one row)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family GPUs.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Workgroup barrier for LDS data written with ds_write: drain this wave's LDS
+// traffic, then s_barrier.  (No memory fence: the direct-to-LDS loads are
+// waited for explicitly with vmcnt, so no blanket vmcnt(0) is wanted here.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
 }
 
-__device__ __forceinline__ float wave_sum16(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m)); }
+__device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
+
+// 8 FP8 E4M3FN codes (two dwords) -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 raw) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// 16 FP8 E4M3FN codes -> 16 bf16 values (exact), as two 16-byte vectors.
-__device__ __forceinline__ void fp8x16_to_bf16(u32x4 raw, u32x4& lo, u32x4& hi) {
-  uint32_t o[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[k], 1.0f, false);
-    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[k], 1.0f, true);
-    o[2 * k] = __builtin_bit_cast(uint32_t, a);
-    o[2 * k + 1] = __builtin_bit_cast(uint32_t, b);
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool FP8>
+struct KvGeom {
+  static constexpr int kEsz = FP8 ? 1 : 2;
+  static constexpr int kRowB = kLatent * kEsz;        // bytes per position (HBM and LDS)
+  static constexpr int kChunksPerRow = kRowB / 16;    // 36 or 72
+  static constexpr int kPageB = kPage * kRowB;        // 9216 or 18432
+  static constexpr int kLoadsPerPage = kPageB / 1024; // wave-wide 1 KiB DMA loads: 9 or 18
+  static constexpr int kTileB = kTilePages * kPageB;
+  static constexpr int kNBuf = FP8 ? 3 : 2;
+  // XOR applied to the 16-byte chunk index of a row.  Rows are 144 (FP8) or
+  // 288 (bf16) dwords apart, so rows r and r+4 (FP8) or r and r+2 (bf16) start
+  // on the same LDS bank; the XOR separates exactly those rows, which makes a
+  // 16-lane access to one chunk of 16 consecutive rows conflict-free.
+  static __device__ __forceinline__ int swz(int row) { return FP8 ? (row >> 2) & 3 : (row >> 1) & 7; }
+  // LDS byte offset (inside a page) of byte `inner` of logical 16-byte chunk x of row `row`.
+  static __device__ __forceinline__ int off(int row, int x, int inner) {
+    return (row * kChunksPerRow + (x ^ swz(row))) * 16 + inner;
   }
-  lo = u32x4{o[0], o[1], o[2], o[3]};
-  hi = u32x4{o[4], o[5], o[6], o[7]};
+};
+
+// Raw value operand: 8 consecutive positions t0..t0+7 of column (cb + lane % 16),
+// from a 16-lane group's transposed LDS read; vop() converts it.  `tile` is
+// the LDS tile base, t0 a multiple of 8, cb a multiple of 16, s = lane % 16.
+template <bool FP8>
+__device__ __forceinline__ typename std::conditional<FP8, u32x2, u32x4>::type load_v8(
+    const uint8_t* tile, int t0, int cb, int s) {
+  using G = KvGeom<FP8>;
+  if constexpr (FP8) {
+    // source lane s: position t0 + s/2, byte half s%2 of the 16 columns cb..cb+15
+    const int t = t0 + (s >> 1);
+    const uint8_t* p = tile + (t >> 4) * G::kPageB + G::off(t & 15, cb >> 4, 8 * (s & 1));
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, p)));
+  } else {
+    // source lane s: position t0 + s/4 (and +4), columns cb + 4(s%4) .. +3
+    const int cbyte = 2 * cb + 8 * (s & 3);
+    const int t = t0 + (s >> 2);
+    const uint8_t* p0 = tile + (t >> 4) * G::kPageB + G::off(t & 15, cbyte >> 4, cbyte & 15);
+    const int t4 = t + 4;
+    const uint8_t* p1 = tile + (t4 >> 4) * G::kPageB + G::off(t4 & 15, cbyte >> 4, cbyte & 15);
+    const u32x2 u0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p0)));
+    const u32x2 u1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p1)));
+    return u32x4{u0[0], u0[1], u1[0], u1[1]};
+  }
 }
 
-template <int NQ, bool FP8, bool FINAL>
-__global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
-  // Query row tiles kept in LDS instead of registers: with bf16 pages the
-  // 72-register staging buffer does not fit beside three register-resident
-  // query tiles, so the last tile is read from LDS at each k-step instead.
-  constexpr int QL = (!FP8 && NQ == 3) ? 1 : 0;
-  constexpr int QR = NQ - QL;
-  // 16-byte chunks of one page: 576 B (fp8) or 1152 B (bf16) per position.
-  constexpr int kEsz = FP8 ? 1 : 2;
-  constexpr int kPageBytes = kPage * kLatent * kEsz;
-  constexpr int kChunksPerRow = kLatent * kEsz / 16;   // 36 or 72
-  constexpr int kChunks = kPageBytes / 16 / 64;        // per lane: 9 or 18
+// Raw key operand: dims d0..d0+7 (d0 a multiple of 8) of position `row` of
+// `page`: 8 FP8 bytes or 8 bf16 values, converted by kop() right before use so
+// the LDS latency overlaps the previous MFMAs.
+template <bool FP8>
+struct KRaw {
+  using T = typename std::conditional<FP8, u32x2, u32x4>::type;
+};
+template <bool FP8>
+__device__ __forceinline__ typename KRaw<FP8>::T load_k8(const uint8_t* page, int row, int d0) {
+  using G = KvGeom<FP8>;
+  const int byte = d0 * G::kEsz;
+  return *(const typename KRaw<FP8>::T*)(page + G::off(row, byte >> 4, byte & 15));
+}
+__device__ __forceinline__ bf16x8 kop(u32x2 raw) { return fp8x8_to_bf16(raw); }
+__device__ __forceinline__ bf16x8 kop(u32x4 raw) { return as_bf16x8(raw); }
 
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kTilePos * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[NQ * 16 * kPRowB];
-  __shared__ float red_max[kWaves][NQ * 16];
-  __shared__ float red_sum[kWaves][NQ * 16];
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[QL > 0 ? QL * 16 * kRowB : 16];
+// Software-pipelined operand stream: load(i) issues the LDS read of step i,
+// use(i, raw) converts and consumes it.  Steps are grouped GRP at a time; the
+// reads of group n+1 are issued before the MFMAs of group n, and a scheduling
+// barrier keeps the compiler from hoisting further reads (register pressure).
+template <int N, int GRP, typename Raw, typename LoadF, typename UseF>
+__device__ __forceinline__ void pipelined(LoadF&& load, UseF&& use) {
+  static_assert(N % GRP == 0, "group size must divide the step count");
+  Raw cur[GRP], nxt[GRP];
+#pragma unroll
+  for (int j = 0; j < GRP; ++j) cur[j] = load(j);
+#pragma unroll
+  for (int gi = 0; gi < N / GRP; ++gi) {
+    if (gi + 1 < N / GRP) {
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) nxt[j] = load((gi + 1) * GRP + j);
+    }
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) use(gi * GRP + j, cur[j]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) cur[j] = nxt[j];
+  }
+}
+
+template <int LAYOUT, bool FP8, bool FINAL>
+__global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using G = KvGeom<FP8>;
+  using KR = typename KRaw<FP8>::T;
+  constexpr bool L16 = LAYOUT == kLayout16;
+  // Tile: 64 positions (4 pages), except 32 (2 pages) for bf16 with 48 rows,
+  // where LDS holds three bf16 tiles plus the partial-score exchange.
+  constexpr int TP = (!L16 && !FP8) ? 32 : 64;
+  constexpr int TPG = TP / kPage;                  // pages per tile
+  constexpr int kTileB = TPG * G::kPageB;
+  constexpr int kNBuf = L16 ? G::kNBuf : 3;
+  constexpr int kWaveLoads = kTileB / kWaves / 1024;   // 1 KiB DMA loads per wave per tile (9 or 18)
+  constexpr int RPAD = L16 ? 16 : 48;
+  constexpr int kPRB = TP * 2 + 16;                // LDS bytes per probability row
+  constexpr int NS32 = TP / 32;                    // 32-position sub-tiles of the 32-row tile
+  constexpr int NS16 = TP / 16;                    // 16-position sub-tiles of the 16-row tile
+  constexpr int kQRegs = 18;                       // query fragments held per wave
+  constexpr int kXFloats = L16 ? 1 : 16 * NS32;    // partial scores exchanged per lane
+  // Lazy rescale: a row's reference maximum moves only when a tile maximum
+  // exceeds it by more than 2^kSlack (bf16 probabilities up to 2^8 are exact
+  // enough and far from overflow), which skips most output rescales.
+  constexpr float kSlack = 8.f;
+
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[RPAD * kPRB];
+  __shared__ float red_max[kWaves][RPAD];
+  __shared__ float red_sum[kWaves][RPAD];
+  __shared__ __attribute__((aligned(16))) float xbuf[L16 ? 4 : kWaves * kXFloats * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15;
+  const int g = lane >> 4;       // 16-lane group
+  const int r32 = lane & 31;
+  const int h = lane >> 5;       // 32-lane half
+  const int dh = w & 1;          // layout 48: which half of the 576 dims this wave contracts
+  const bool t32 = !L16 && w < 2;  // layout 48: wave works on the 32-row tile
   const int split = blockIdx.x;
   const int b = blockIdx.y;
+  const int H = a.heads;
+  const int R = a.num_q * H;
+
+  const int L = a.seq_lens[b];
+  const int P = (L + kPage - 1) / kPage;
+  const int p0 = (int)(((int64_t)split * P) / a.num_splits);
+  const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
+  const int ntiles = (p1 - p0 + TPG - 1) / TPG;
+  // read-only page table through the constant address space: uniform
+  // indices become scalar loads, which do not count against vmcnt
+  const __attribute__((address_space(4))) int32_t* pt_row =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + (int64_t)b * a.max_blocks);
+
+  // Rows owned by this lane: A = the 32-row tile row (layout 48) or the 16-row
+  // tile row (layout 16); B = the 16-row tile row 32 + r16 (layout 48).
+  const int rowA = L16 ? r16 : r32;
+  const int rowB = 32 + r16;
+  const int limA = L - a.num_q + rowA / H + 1;   // visible: position < lim
+  const int limB = L - a.num_q + rowB / H + 1;
+
+  // ---- query fragments (B operand of S^T = K Q^T), kept in registers.
+  //      layout 16:             row r16,      dims 32ks + 8g,          ks < 18
+  //      layout 48, waves 0/1:  row r32,      dims 288dh + 16ks + 8h,  ks < 18
+  //      layout 48, waves 2/3:  row 32 + r16, dims 288dh + 32ks + 8g,  ks < 9
+  u32x4 qreg[kQRegs];
+  {
+    const int qrow = L16 ? r16 : (t32 ? r32 : rowB);
+    const bool real = qrow < R;
+    const uint16_t* qp = a.q + ((int64_t)b * R + (real ? qrow : 0)) * kLatent;
+#pragma unroll
+    for (int ks = 0; ks < kQRegs; ++ks) {
+      int d0;
+      if (L16) d0 = 32 * ks + 8 * g;
+      else d0 = t32 ? 288 * dh + 16 * ks + 8 * h : 288 * dh + 32 * (ks % 9) + 8 * g;
+      const bool use = real && (L16 || t32 || ks < 9);
+      qreg[ks] = use ? *(const u32x4*)(qp + d0) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  float m_runA = kNegInf, l_runA = 0.f, m_runB = kNegInf, l_runB = 0.f;
+  constexpr int kN16a = L16 ? 8 : 1;   // layout 16: 8 tiles of 16 columns
+  constexpr int kN32 = L16 ? 1 : 4;    // layout 48: 32-row tile, 4 x 32 columns
+  constexpr int kN16b = L16 ? 1 : 8;   // layout 48: 16-row tile, 8 x 16 columns
+  f32x4 o16a[kN16a];
+  f32x16 o32[kN32];
+  f32x4 o16b[kN16b];
+#pragma unroll
+  for (int c = 0; c < kN16a; ++c) o16a[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kN32; ++c) o32[c] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < kN16b; ++c) o16b[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- a2: tile T -> LDS buffer T % NBUF.  Wave w copies 1 KiB DMA loads
+  // [w * kWaveLoads, (w+1) * kWaveLoads) of the tile: one page, or half a page
+  // for 32-position bf16 tiles.  Lane `lane` of a load fills the LDS slot
+  // (row, x ^ (row & swz)) of its page and fetches logical chunk x of that row.
+  constexpr int kWavesPerPage = kWaves / TPG;     // 1 or 2
+  const int wpage = w / kWavesPerPage;            // tile page this wave copies
+  const int wslot0 = (w % kWavesPerPage) * kWaveLoads * 64;  // first 16-byte slot in that page
+  auto issue_tile = [&](int T) {
+    uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + wpage * G::kPageB + wslot0 * 16;
+    const int page = p0 + T * TPG + wpage;
+    if (page < p1) {
+      // one buffer resource per page: the copy is bounds-checked to the page
+      const int blk = __builtin_amdgcn_readfirstlane(pt_row[page]);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.kv + (int64_t)blk * G::kPageB), 0, G::kPageB, kBufferRsrcWord3);
+#pragma unroll
+      for (int c = 0; c < kWaveLoads; ++c) {
+        const uint32_t slot = wslot0 + 64 * c + lane;
+        const uint32_t row = slot / G::kChunksPerRow;
+        const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16,
+                                                 row * G::kRowB + x * 16, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kWaveLoads; ++c)
+        *(u32x4*)(dst + 1024 * c + 16 * lane) = u32x4{0, 0, 0, 0};
+    }
+  };
+  auto has_page = [&](int T) { return p0 + T * TPG + wpage < p1; };
+
+#pragma unroll
+  for (int T = 0; T < kNBuf - 1; ++T)
+    if (T < ntiles) issue_tile(T);
+
+  const float c2 = a.score_scale_log2;
+
+  for (int it = 0; it < ntiles; ++it) {
+    // Wait for this wave's copy of tile `it`; a later tile may stay in flight.
+    if (kNBuf == 3 && it + 1 < ntiles && has_page(it + 1))
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    uint8_t* tile = kv_lds + (it % kNBuf) * kTileB;
+    {
+      // zero the slots past seq_len among the rows this wave copied (last page only)
+      const int page = p0 + it * TPG + wpage;
+      const int valid = L - page * kPage;
+      constexpr int kRowsPerWave = kPage / kWavesPerPage;
+      const int row0 = (w % kWavesPerPage) * kRowsPerWave;
+      const int z0 = valid > row0 ? valid : row0;
+      if (page < p1 && z0 < row0 + kRowsPerWave) {
+        uint8_t* pg = tile + wpage * G::kPageB;
+        for (int c = lane; c < (row0 + kRowsPerWave - z0) * G::kChunksPerRow; c += 64)
+          *(u32x4*)(pg + (z0 * G::kChunksPerRow + c) * 16) = u32x4{0, 0, 0, 0};
+      }
+    }
+    lds_barrier();  // tile `it` visible; every wave is done with tile it - 1
+    if (it + kNBuf - 1 < ntiles) issue_tile(it + kNBuf - 1);
+
+    const int tpos0 = (p0 + it * TPG) * kPage;      // sequence position of tile slot 0
+    const int tlim = (p1 - p0 - it * TPG) * kPage;  // tile slots inside the split
+
+    float alphaA = 1.f, alphaB = 1.f;
+    if constexpr (L16) {
+      // ---- a4/a5 (<= 16 rows): wave w scores page w of the tile against the 16-row tile.
+      float sv[4];
+      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      const uint8_t* pg = tile + w * G::kPageB;
+      pipelined<18, 3, KR>([&](int ks) { return load_k8<FP8>(pg, r16, 32 * ks + 8 * g); },
+                           [&](int ks, KR raw) {
+                             if (ks & 1) s1 = mfma16(kop(raw), as_bf16x8(qreg[ks]), s1);
+                             else s0 = mfma16(kop(raw), as_bf16x8(qreg[ks]), s0);
+                           });
+      const f32x4 s = s0 + s1;
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = 16 * w + 4 * g + i;
+        const bool ok = tt < tlim && tpos0 + tt < limA;
+        sv[i] = ok ? s[i] * c2 : kNegInf;
+        mx = fmaxf(mx, sv[i]);
+      }
+      mx = xor_max(xor_max(mx, 16), 32);
+      if (g == 0) red_max[w][r16] = mx;
+      lds_barrier();
+
+      const float mt = fmaxf(fmaxf(red_max[0][r16], red_max[1][r16]), fmaxf(red_max[2][r16], red_max[3][r16]));
+      const float mA = (mt > m_runA + kSlack) ? mt : m_runA;   // lazy rescale
+      alphaA = (mA == m_runA) ? 1.f : __builtin_amdgcn_exp2f(m_runA - mA);
+      m_runA = mA;
+      bf16x4 pb;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = (sv[i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - mA);
+        pb[i] = (__bf16)p;
+        ps += p;
+      }
+      ps = xor_sum(xor_sum(ps, 16), 32);
+      if (g == 0) red_sum[w][r16] = ps;
+      *(bf16x4*)(p_lds + r16 * kPRB + (16 * w + 4 * g) * 2) = pb;
+      lds_barrier();
+      l_runA = l_runA * alphaA + ((red_sum[0][r16] + red_sum[1][r16]) + (red_sum[2][r16] + red_sum[3][r16]));
+    } else {
+      // ---- a4 (17..48 rows): the wave pair of a row tile splits the 576 dims in
+      // halves; partial scores of every tile position are swapped through LDS.
+      float* xme = xbuf + w * kXFloats * 64;
+      const float* xpeer = xbuf + (w ^ 1) * kXFloats * 64;
+      if (t32) {
+        f32x16 s[NS32];
+#pragma unroll
+        for (int sp = 0; sp < NS32; ++sp) s[sp] = f32x16{};
+        // step i: k-step i % 18 of sub-tile i / 18
+        pipelined<18 * NS32, 3, KR>(
+            [&](int i) {
+              const int tt = 32 * (i / 18) + r32;
+              return load_k8<FP8>(tile + (tt >> 4) * G::kPageB, tt & 15, 288 * dh + 16 * (i % 18) + 8 * h);
+            },
+            [&](int i, KR raw) { s[i / 18] = mfma32(kop(raw), as_bf16x8(qreg[i % 18]), s[i / 18]); });
+#pragma unroll
+        for (int sp = 0; sp < NS32; ++sp)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(f32x4*)(xme + ((sp * 4 + q) * 64 + lane) * 4) =
+                f32x4{s[sp][4 * q], s[sp][4 * q + 1], s[sp][4 * q + 2], s[sp][4 * q + 3]};
+        lds_barrier();
+        float sv[16 * NS32];
+        float mx = kNegInf;
+#pragma unroll
+        for (int sp = 0; sp < NS32; ++sp)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 pv = *(const f32x4*)(xpeer + ((sp * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tq = 32 * sp + 8 * q + 4 * h + i;
+              const bool ok = tq < tlim && tpos0 + tq < limA;
+              const float v = ok ? (s[sp][4 * q + i] + pv[i]) * c2 : kNegInf;
+              sv[16 * sp + 4 * q + i] = v;
+              mx = fmaxf(mx, v);
+            }
+          }
+        mx = xor_max(mx, 32);
+        const float mA = (mx > m_runA + kSlack) ? mx : m_runA;   // lazy rescale
+        if (w == 0 && h == 0) red_max[0][r32] = mA;
+        // this wave writes the probabilities of its half of the tile positions
+        float ps = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8 * NS32; k += 4) {
+          const int base = (NS32 == 2) ? 16 * dh + k : 8 * dh + k;  // sv index of a 4-run
+          bf16x4 pb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = sv[base + i];
+            const float p = (v == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(v - mA);
+            pb[i] = (__bf16)p;
+            ps += p;
+          }
+          const int sp = base / 16, q = (base % 16) / 4;
+          *(bf16x4*)(p_lds + r32 * kPRB + (32 * sp + 8 * q + 4 * h) * 2) = pb;
+        }
+        ps = xor_sum(ps, 32);
+        if (h == 0) red_sum[w][r32] = ps;
+      } else {
+        f32x4 s[NS16];
+#pragma unroll
+        for (int sp = 0; sp < NS16; ++sp) s[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // step i: k-step i % 9 of sub-tile i / 9
+        pipelined<9 * NS16, 3, KR>(
+            [&](int i) {
+              return load_k8<FP8>(tile + (i / 9) * G::kPageB, r16, 288 * dh + 32 * (i % 9) + 8 * g);
+            },
+            [&](int i, KR raw) { s[i / 9] = mfma16(kop(raw), as_bf16x8(qreg[i % 9]), s[i / 9]); });
+#pragma unroll
+        for (int sp = 0; sp < NS16; ++sp) *(f32x4*)(xme + (sp * 64 + lane) * 4) = s[sp];
+        lds_barrier();
+        float sv[4 * NS16];
+        float mx = kNegInf;
+#pragma unroll
+        for (int sp = 0; sp < NS16; ++sp) {
+          const f32x4 pv = *(const f32x4*)(xpeer + (sp * 64 + lane) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tq = 16 * sp + 4 * g + i;
+            const bool ok = tq < tlim && tpos0 + tq < limB;
+            const float v = ok ? (s[sp][i] + pv[i]) * c2 : kNegInf;
+            sv[4 * sp + i] = v;
+            mx = fmaxf(mx, v);
+          }
+        }
+        mx = xor_max(xor_max(mx, 16), 32);
+        const float mB = (mx > m_runB + kSlack) ? mx : m_runB;   // lazy rescale
+        if (w == 2 && g == 0) red_max[2][rowB] = mB;
+        float ps = 0.f;
+#pragma unroll
+        for (int k = 0; k < NS16 / 2; ++k) {
+          const int sp = dh * (NS16 / 2) + k;
+          bf16x4 pb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = sv[4 * sp + i];
+            const float p = (v == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(v - mB);
+            pb[i] = (__bf16)p;
+            ps += p;
+          }
+          *(bf16x4*)(p_lds + rowB * kPRB + (16 * sp + 4 * g) * 2) = pb;
+        }
+        ps = xor_sum(xor_sum(ps, 16), 32);
+        if (g == 0) red_sum[w][rowB] = ps;
+      }
+      lds_barrier();
+      // every wave tracks both row tiles (it holds their outputs for its columns)
+      const float mA = red_max[0][r32];
+      alphaA = (mA == m_runA) ? 1.f : __builtin_amdgcn_exp2f(m_runA - mA);
+      m_runA = mA;
+      l_runA = l_runA * alphaA + (red_sum[0][r32] + red_sum[1][r32]);
+      const float mB = red_max[2][rowB];
+      alphaB = (mB == m_runB) ? 1.f : __builtin_amdgcn_exp2f(m_runB - mB);
+      m_runB = mB;
+      l_runB = l_runB * alphaB + (red_sum[2][rowB] + red_sum[3][rowB]);
+    }
+
+    // ---- output rescale, only when some row's maximum moved.
+    if (__any(alphaA != 1.f || alphaB != 1.f)) {
+      if constexpr (L16) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o16a[c] *= alphaA;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o32[c] *= alphaA;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o16b[c] *= alphaB;
+      }
+    }
+
+    // ---- a6: O^T[c][r] += V^T[c][t] P^T[t][r] for this wave's 128 columns.
+    const int col0 = 128 * w;
+    if constexpr (L16) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pf[kk] = as_bf16x8(*(const u32x4*)(p_lds + r16 * kPRB + (32 * kk + 8 * g) * 2));
+      // step i: k-step i/8 (32 positions), column tile i%8
+      pipelined<16, 4, KR>(
+          [&](int i) { return load_v8<FP8>(tile, 32 * (i >> 3) + 8 * g, col0 + 16 * (i & 7), r16); },
+          [&](int i, KR raw) { o16a[i & 7] = mfma16(kop(raw), pf[i >> 3], o16a[i & 7]); });
+    } else {
+      constexpr int K32 = TP / 16;   // 16-position k-steps of the 32-row tile
+      constexpr int K16 = TP / 32;   // 32-position k-steps of the 16-row tile
+      bf16x8 pf32[K32], pf16[K16];
+#pragma unroll
+      for (int kk = 0; kk < K32; ++kk)
+        pf32[kk] = as_bf16x8(*(const u32x4*)(p_lds + r32 * kPRB + (16 * kk + 8 * h) * 2));
+#pragma unroll
+      for (int kk = 0; kk < K16; ++kk)
+        pf16[kk] = as_bf16x8(*(const u32x4*)(p_lds + rowB * kPRB + (32 * kk + 8 * g) * 2));
+      // steps [0, 4*K32): 32-row tile, k-step i/4 (16 positions), column tile i%4 (32 columns);
+      // then 8*K16 steps: 16-row tile, k-step j/8 (32 positions), column tile j%8.
+      pipelined<4 * K32 + 8 * K16, 4, KR>(
+          [&](int i) {
+            if (i < 4 * K32)
+              return load_v8<FP8>(tile, 16 * (i >> 2) + 8 * h, col0 + 32 * (i & 3) + 16 * (g & 1), r16);
+            const int j = i - 4 * K32;
+            return load_v8<FP8>(tile, 32 * (j >> 3) + 8 * g, col0 + 16 * (j & 7), r16);
+          },
+          [&](int i, KR raw) {
+            if (i < 4 * K32) {
+              o32[i & 3] = mfma32(kop(raw), pf32[i >> 2], o32[i & 3]);
+            } else {
+              const int j = i - 4 * K32;
+              o16b[j & 7] = mfma16(kop(raw), pf16[j >> 3], o16b[j & 7]);
+            }
+          });
+    }
+  }
+
+  // ---- a7: epilogue (real rows only).
+  const int64_t row_base = (int64_t)b * R;
+  auto store4 = [&](int r, int col, f32x4 v, float sc) {
+    const int64_t orow = row_base + r;
+    if constexpr (FINAL) {
+      bf16x4 ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(v[i] * sc);
+      *(bf16x4*)(a.out + orow * kValue + col) = ov;
+    } else {
+      const int64_t prow = (int64_t)split * a.batch * R + orow;
+      *(f32x4*)(a.part_out + prow * kValue + col) = v * sc;
+    }
+  };
+  auto store_lse = [&](int r, float m_run, float l_run) {
+    const float v = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
+    const int64_t orow = row_base + r;
+    if constexpr (FINAL) a.lse[orow] = v;
+    else a.part_lse[(int64_t)split * a.batch * R + orow] = v;
+  };
+  const float scA = l_runA > 0.f ? a.out_scale / l_runA : 0.f;
+  const int col0 = 128 * w;
+  if constexpr (L16) {
+    if (r16 < R) {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) store4(r16, col0 + 16 * ct + 4 * g, o16a[ct], scA);
+      if (w == 0 && g == 0) store_lse(r16, m_runA, l_runA);
+    }
+  } else {
+    if (r32 < R) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v{o32[ct][4 * q], o32[ct][4 * q + 1], o32[ct][4 * q + 2], o32[ct][4 * q + 3]};
+          store4(r32, col0 + 32 * ct + 8 * q + 4 * h, v, scA);
+        }
+      if (w == 0 && h == 0) store_lse(r32, m_runA, l_runA);
+    }
+    if (rowB < R) {
+      const float scB = l_runB > 0.f ? a.out_scale / l_runB : 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) store4(rowB, col0 + 16 * ct + 4 * g, o16b[ct], scB);
+      if (w == 0 && g == 0) store_lse(rowB, m_runB, l_runB);
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---------------------------------------------------------------------------
+// FP8 KV with 33..64 query rows (speculative verify): the FP8 latents are fed
+// to the 32x32x64 FP8 MFMA as stored, with no decode.  The bf16 side of each
+// product is written as a sum of two FP8 terms:
+//   query:         q * 2^e = q1 + q2, e chosen per row so max|q * 2^e| is in
+//                  [64, 128); q has 8 significant bits and the residual of the
+//                  first RNE rounding fits the second term, so q1 + q2 equals
+//                  q * 2^e up to 2^-10 absolute, i.e. 2^-16 of the row maximum;
+//   probabilities: p * 2^8 = p1 + p2, accurate to 2^-8 relative (bf16 gives
+//                  2^-9), while the softmax denominator keeps the fp32 p.
+// Each product therefore takes two FP8 MFMAs, which cost what one bf16 MFMA of
+// the same shape costs, and no VALU conversion touches the KV stream.
+// Rows are two 32-row tiles (r = j*H + h); wave w owns row tile w/2 and the
+// 32-position half w%2 of every 64-position tile; PV is column-split as above.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  // formats 0/0 = FP8 E4M3 for both operands; E8M0 scales 127 = 1.0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// four fp32 values -> (RNE FP8 of each, RNE FP8 of each residual), packed 4 per dword
+__device__ __forceinline__ void split4_fp8(float v0, float v1, float v2, float v3, int& hi, int& lo) {
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, hi, true);
+  const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0 - b01[0], v1 - b01[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v2 - b23[0], v3 - b23[1], lo, true);
+}
+
+template <bool FINAL>
+__global__ __launch_bounds__(kThreads, 1) void split_kernel_f8x64(SplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using G = KvGeom<true>;
+  constexpr int kNBuf = 3;
+  constexpr int kTileB = kTilePages * G::kPageB;          // 36,864
+  constexpr int kWaveLoads = G::kPageB / 1024;            // 9: wave w copies page w
+  constexpr int kPRB = kTilePos + 16;                     // bytes per FP8 probability row (+skew)
+  constexpr float kSlack = 4.f;                           // log2 headroom of the lazy rescale
+  constexpr float kPScale = 16.f;                         // 2^(8 - kSlack)
+
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2 * 64 * kPRB];  // [term][row][position]
+  __shared__ float red_max[kWaves][32];
+  __shared__ float red_sum[kWaves][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const int rt = w >> 1;         // row tile: rows 32*rt .. 32*rt + 31
+  const int sp = w & 1;          // tile positions 32*sp .. 32*sp + 31
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int H = a.heads;
+  const int R = a.num_q * H;
 
   const int L = a.seq_lens[b];
   const int P = (L + kPage - 1) / kPage;
   const int p0 = (int)(((int64_t)split * P) / a.num_splits);
   const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
   const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
-  const int32_t* pt_row = a.page_table + (int64_t)b * a.max_blocks;
+  // read-only page table through the constant address space: uniform
+  // indices become scalar loads, which do not count against vmcnt
+  const __attribute__((address_space(4))) int32_t* pt_row =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + (int64_t)b * a.max_blocks);
 
-  // ---- query fragments (B operand of S^T = K Q^T): row n = head r16, k = d.
-  bf16x8 qf[QR > 0 ? QR : 1][kKSteps];
-#pragma unroll
-  for (int j = 0; j < QR; ++j) {
-    const bool real = r16 < a.heads;
-    const uint16_t* qrow = a.q + (((int64_t)b * a.num_q + j) * a.heads + (real ? r16 : 0)) * kLatent;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      u32x4 v = real ? *(const u32x4*)(qrow + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
-      qf[j][ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  const int myrow = 32 * rt + r32;
+  const int lim = L - a.num_q + myrow / H + 1;   // visible: position < lim
 
-  if constexpr (QL > 0) {
-    // rows 16 * (j - QR) + h of q_lds hold token j >= QR; pad rows are zero.
-    for (int c = tid; c < QL * 16 * (kLatent / 8); c += kThreads) {
-      const int row = c / (kLatent / 8);
-      const int col = c % (kLatent / 8);
-      const int j = QR + row / 16, h = row % 16;
-      u32x4 v{0, 0, 0, 0};
-      if (h < a.heads) v = *(const u32x4*)(a.q + (((int64_t)b * a.num_q + j) * a.heads + h) * kLatent + 8 * col);
-      *(u32x4*)(q_lds + row * kRowB + 16 * col) = v;
-    }
-  }
-
-  float m_run[NQ], l_run[NQ];
-  f32x4 o[NQ][kColTiles];
+  float m_run0 = kNegInf, l_run0 = 0.f, m_run1 = kNegInf, l_run1 = 0.f;
+  f32x16 o[2][4];
 #pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    m_run[j] = kNegInf;
-    l_run[j] = 0.f;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) o[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int c = 0; c < 4; ++c) o[t][c] = f32x16{};
 
-  // ---- a2: page gather into registers (one tile ahead).
-  u32x4 stg[kChunks];
-  auto load_tile = [&](int it) {
-    const int page = p0 + it * kTilePages + w;
+  // ---- a2: tile T -> LDS buffer T % 3; wave w copies page w of the tile.
+  auto issue_tile = [&](int T) {
+    uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + w * G::kPageB;
+    const int page = p0 + T * kTilePages + w;
     if (page < p1) {
-      const int blk = pt_row[page];
-      const uint8_t* src = a.kv + (int64_t)blk * kPageBytes;
+      const int blk = __builtin_amdgcn_readfirstlane(pt_row[page]);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.kv + (int64_t)blk * G::kPageB), 0, G::kPageB, kBufferRsrcWord3);
+      // recompute the per-lane offsets at every copy instead of keeping nine
+      // loop-invariant registers alive across the whole loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) stg[c] = *(const u32x4*)(src + (lane + 64 * c) * 16);
-    }
-  };
-  auto store_tile = [&](int it) {
-    const int page = p0 + it * kTilePages + w;
-    const bool have = page < p1;
-    const int valid_rows = have ? min(kPage, L - page * kPage) : 0;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int chunk = lane + 64 * c;
-      const int row = chunk / kChunksPerRow;
-      const int col = chunk % kChunksPerRow;
-      const bool ok = row < valid_rows;
-      uint8_t* dst = kv_lds + (w * kPage + row) * kRowB;
-      if constexpr (FP8) {
-        u32x4 lo, hi;
-        fp8x16_to_bf16(stg[c], lo, hi);
-        const u32x4 z{0, 0, 0, 0};
-        *(u32x4*)(dst + col * 32) = ok ? lo : z;
-        *(u32x4*)(dst + col * 32 + 16) = ok ? hi : z;
-      } else {
-        *(u32x4*)(dst + col * 16) = ok ? stg[c] : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < kWaveLoads; ++c) {
+        const uint32_t slot = 64 * c + ln;
+        const uint32_t row = slot / G::kChunksPerRow;
+        const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16,
+                                                 row * G::kRowB + x * 16, 0, 0, 0);
       }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kWaveLoads; ++c)
+        *(u32x4*)(dst + 1024 * c + 16 * lane) = u32x4{0, 0, 0, 0};
     }
   };
+  auto has_page = [&](int T) { return p0 + T * kTilePages + w < p1; };
 
-  if (ntiles > 0) load_tile(0);
+#pragma unroll
+  for (int T = 0; T < kNBuf - 1; ++T)
+    if (T < ntiles) issue_tile(T);
+
+  // The first copies are in flight while the query is prepared.
+  // ---- query: q * 2^e = q1 + q2 (FP8), dims 64ks + 32h + j of row `myrow`.
+  i32x8 q1[9], q2[9];
+  float q_unscale;
+  {
+    const bool real = myrow < R && ntiles > 0;   // empty splits skip the query work
+    const uint16_t* qp = a.q + ((int64_t)b * R + (real ? myrow : 0)) * kLatent + 32 * h;
+    float mx = 0.f;
+    if (real) {
+#pragma unroll
+      for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 v = *(const u32x4*)(qp + 64 * ks + 8 * c);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[k])), fabsf(bf16_hi(v[k]))));
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));            // the two lanes holding this row
+    int e = 0;
+    if (mx > 0.f) {
+      const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126;  // mx = m * 2^ex, m in [0.5, 1)
+      e = min(max(7 - ex, -100), 100);
+    }
+    const float sc = pow2f(e);
+    q_unscale = pow2f(-e);
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      i32x8 hi8, lo8;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = real ? *(const u32x4*)(qp + 64 * ks + 8 * c) : u32x4{0, 0, 0, 0};
+        int hh, ll;
+        split4_fp8(bf16_lo(v[0]) * sc, bf16_hi(v[0]) * sc, bf16_lo(v[1]) * sc, bf16_hi(v[1]) * sc, hh, ll);
+        hi8[2 * c] = hh;
+        lo8[2 * c] = ll;
+        split4_fp8(bf16_lo(v[2]) * sc, bf16_hi(v[2]) * sc, bf16_lo(v[3]) * sc, bf16_hi(v[3]) * sc, hh, ll);
+        hi8[2 * c + 1] = hh;
+        lo8[2 * c + 1] = ll;
+      }
+      q1[ks] = hi8;
+      q2[ks] = lo8;
+    }
+  }
+
+
+  const float cs = a.score_scale_log2 * q_unscale;
 
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();  // previous tile's readers are done with kv_lds / p_lds / red_sum
-    store_tile(it);
-    if (it + 1 < ntiles) load_tile(it + 1);
-    __syncthreads();  // tile visible to all waves
-
-    // ---- a4: S^T for this wave's page, all query rows.
-    f32x4 sacc[NQ];
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* krow = kv_lds + (w * kPage + r16) * kRowB + 16 * g;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8 kf = *(const bf16x8*)(krow + 64 * ks);
-#pragma unroll
-      for (int j = 0; j < QR; ++j)
-        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[j][ks], sacc[j], 0, 0, 0);
-#pragma unroll
-      for (int j = QR; j < NQ; ++j) {
-        const bf16x8 qv = *(const bf16x8*)(q_lds + ((j - QR) * 16 + r16) * kRowB + 16 * g + 64 * ks);
-        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv, sacc[j], 0, 0, 0);
+    if (it + 1 < ntiles && has_page(it + 1))
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    uint8_t* tile = kv_lds + (it % kNBuf) * kTileB;
+    {
+      const int page = p0 + it * kTilePages + w;
+      const int valid = L - page * kPage;
+      if (page < p1 && valid < kPage) {
+        uint8_t* pg = tile + w * G::kPageB;
+        for (int c = lane; c < (kPage - valid) * G::kChunksPerRow; c += 64)
+          *(u32x4*)(pg + (valid * G::kChunksPerRow + c) * 16) = u32x4{0, 0, 0, 0};
       }
     }
+    lds_barrier();  // tile `it` visible; every wave is done with tile it - 1
+    if (it + kNBuf - 1 < ntiles) issue_tile(it + kNBuf - 1);
 
-    // ---- a5: mask, scale (log2 domain), tile row maxima.
-    const int page = p0 + it * kTilePages + w;
-    const int t0 = page * kPage + 4 * g;
-    float sv[NQ][4];
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int lim = (page < p1) ? (L - a.num_q + j + 1) : 0;  // visible: t < lim
-      float mx = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[j][i] = (t0 + i < lim) ? sacc[j][i] * a.score_scale_log2 : kNegInf;
-        mx = fmaxf(mx, sv[j][i]);
-      }
-      mx = wave_max16(mx);
-      if (g == 0) red_max[w][j * 16 + r16] = mx;
+    const int tpos0 = (p0 + it * kTilePages) * kPage;
+    const int tlim = (p1 - p0 - it * kTilePages) * kPage;
+
+    // ---- a4: S^T for positions 32sp + (0..31) against row tile rt.
+    f32x16 s = f32x16{};
+    {
+      // The swizzle XORs only the low two bits of the chunk index, so chunk
+      // 4ks + c (c < 4) sits at 64ks bytes past chunk c: two lane bases plus
+      // immediate offsets address every k-step.
+      const int prow = r32 & 15;
+      const uint8_t* kb0 = tile + (2 * sp + (r32 >> 4)) * G::kPageB + G::off(prow, 2 * h, 0);
+      const uint8_t* kb1 = tile + (2 * sp + (r32 >> 4)) * G::kPageB + G::off(prow, 2 * h + 1, 0);
+      pipelined<9, 1, i32x8>(
+          [&](int ks) {
+            const u32x4 v0 = *(const u32x4*)(kb0 + 64 * ks);
+            const u32x4 v1 = *(const u32x4*)(kb1 + 64 * ks);
+            return __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+          },
+          [&](int ks, i32x8 kf) {
+            s = mfma_f8(kf, q1[ks], s);
+            s = mfma_f8(kf, q2[ks], s);
+          });
     }
-    __syncthreads();
 
-    float alpha[NQ];
+    // ---- a5: mask (edge tiles only), scale, row maxima (two 32-position halves per row tile).
+    float mx = kNegInf;
+    if (tlim >= kTilePos && tpos0 + kTilePos <= L - a.num_q + 1) {  // every row sees the whole tile
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      float mt = red_max[0][j * 16 + r16];
+      for (int i = 0; i < 16; ++i) {
+        s[i] *= cs;
+        mx = fmaxf(mx, s[i]);
+      }
+    } else {
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) mt = fmaxf(mt, red_max[ww][j * 16 + r16]);
-      const float m_new = fmaxf(m_run[j], mt);
-      alpha[j] = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
-      bf16x4 pb;
+      for (int i = 0; i < 16; ++i) {
+        const int tq = 32 * sp + 8 * (i >> 2) + 4 * h + (i & 3);
+        const bool ok = tq < tlim && tpos0 + tq < lim;
+        s[i] = ok ? s[i] * cs : kNegInf;
+        mx = fmaxf(mx, s[i]);
+      }
+    }
+    mx = xor_max(mx, 32);
+    if (h == 0) red_max[w][r32] = mx;
+    lds_barrier();
+
+    // Lazy rescale: a row's reference maximum moves only when the tile maximum
+    // exceeds it by more than 2^kSlack; probabilities are then at most 2^kSlack
+    // and their FP8 split stays in range (p * 2^(8 - kSlack) <= 256).
+    const float mt0 = fmaxf(red_max[0][r32], red_max[1][r32]);
+    const float mt1 = fmaxf(red_max[2][r32], red_max[3][r32]);
+    const float mn0 = (mt0 > m_run0 + kSlack) ? mt0 : m_run0;
+    const float mn1 = (mt1 > m_run1 + kSlack) ? mt1 : m_run1;
+    const float alpha0 = (mn0 == m_run0) ? 1.f : __builtin_amdgcn_exp2f(m_run0 - mn0);
+    const float alpha1 = (mn1 == m_run1) ? 1.f : __builtin_amdgcn_exp2f(m_run1 - mn1);
+    m_run0 = mn0;
+    m_run1 = mn1;
+    {
+      const float mm = rt ? mn1 : mn0;
       float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = (sv[j][i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sv[j][i] - m_new);
-        pb[i] = (__bf16)p;
-        ps += p;  // fp32 weights: lse stays exact to fp32; the bf16 rounding of the
-                  // MFMA operand only perturbs the output, unbiased (RNE)
+      for (int q = 0; q < 4; ++q) {
+        float p4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = s[4 * q + i];
+          p4[i] = (v == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(v - mm);
+          ps += p4[i];
+        }
+        int hi, lo;
+        split4_fp8(p4[0] * kPScale, p4[1] * kPScale, p4[2] * kPScale, p4[3] * kPScale, hi, lo);
+        const int off = myrow * kPRB + 32 * sp + 8 * q + 4 * h;
+        *(int*)(p_lds + off) = hi;
+        *(int*)(p_lds + 64 * kPRB + off) = lo;
       }
-      ps = wave_sum16(ps);
-      if (g == 0) red_sum[w][j * 16 + r16] = ps;
-      *(bf16x4*)(p_lds + (j * 16 + r16) * kPRowB + (w * kPage + 4 * g) * 2) = pb;
-      m_run[j] = m_new;
+      ps = xor_sum(ps, 32);
+      if (h == 0) red_sum[w][r32] = ps;
     }
-    __syncthreads();
+    lds_barrier();
 
+    l_run0 = l_run0 * alpha0 + (red_sum[0][r32] + red_sum[1][r32]);
+    l_run1 = l_run1 * alpha1 + (red_sum[2][r32] + red_sum[3][r32]);
+    if (__any(alpha0 != 1.f || alpha1 != 1.f)) {
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      float ts = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) ts += red_sum[ww][j * 16 + r16];
-      l_run[j] = l_run[j] * alpha[j] + ts;
-#pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) o[j][ct] *= alpha[j];
-    }
-
-    // ---- a6: O^T[c][r] += V^T[c][t] P^T[t][r] over the tile's 64 positions.
-#pragma unroll
-    for (int kk = 0; kk < kTilePos / 32; ++kk) {
-      bf16x8 pf[NQ];
-#pragma unroll
-      for (int j = 0; j < NQ; ++j)
-        pf[j] = *(const bf16x8*)(p_lds + (j * 16 + r16) * kPRowB + (32 * kk + 8 * g) * 2);
-      // transposed read: lane s of a 16-lane group loads row (s / 4) and
-      // columns 4 * (s % 4) .. +3 of a 4 x 16 block; afterwards lane i holds
-      // column i of the four rows.
-      const int vrow = 32 * kk + 8 * g + (r16 >> 2);
-      const uint8_t* vbase = kv_lds + vrow * kRowB + (w * (kValue / kWaves) + 4 * (lane & 3)) * 2;
-#pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + ct * 32));
-        const i16x4 v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + 4 * kRowB + ct * 32));
-        const u32x2 u0 = __builtin_bit_cast(u32x2, v0);
-        const u32x2 u1 = __builtin_bit_cast(u32x2, v1);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{u0[0], u0[1], u1[0], u1[1]});
-#pragma unroll
-        for (int j = 0; j < NQ; ++j)
-          o[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[j], o[j][ct], 0, 0, 0);
+      for (int c = 0; c < 4; ++c) {
+        o[0][c] *= alpha0;
+        o[1][c] *= alpha1;
       }
+    }
+
+    // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128w .. 128w + 127.
+    // One row tile at a time (the value operand is read twice) keeps the
+    // probability operands to 16 registers.
+    const int g = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      i32x8 pf[2];
+#pragma unroll
+      for (int term = 0; term < 2; ++term) {
+        const uint8_t* pr = p_lds + term * 64 * kPRB + (32 * t + r32) * kPRB + 32 * h;
+        const u32x4 v0 = *(const u32x4*)pr;
+        const u32x4 v1 = *(const u32x4*)(pr + 16);
+        pf[term] = __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      }
+      // step i: column tile ct = i/4, positions 32h + 8e .. +7 with e = i%4 (one
+      // transposed read each).  Source lane s of a 16-lane group reads position
+      // 32h + 8e + s/2, i.e. page 2h + e/2, row 8(e%2) + s/2, byte half s%2 of
+      // chunk 8w + 2ct + (g%2), XOR-swizzled by (row/4)%4 = s/8 + 2(e%2).  Split
+      // into a lane part and a constant part:
+      //   bits 0 of chunk: (g ^ s/8) % 2          (lane)
+      //   bit 1 of chunk:  (ct ^ e) % 2           (constant)
+      //   higher bits:     8w + 4(ct/2)            (constant per wave)
+      u32x2 vraw[4];
+      const int sl = lane & 15;
+      const uint8_t* vb = tile + 2 * h * G::kPageB + (sl >> 1) * G::kRowB +
+                          16 * (8 * w + ((g ^ (sl >> 3)) & 1)) + 8 * (sl & 1);
+      pipelined<16, 4, u32x2>(
+          [&](int i) {
+            const int e = i & 3, ct = i >> 2;
+            const int cst = (e >> 1) * G::kPageB + 8 * (e & 1) * G::kRowB + 16 * (4 * (ct >> 1) + 2 * ((ct ^ e) & 1));
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vb + cst)));
+          },
+          [&](int i, u32x2 raw) {
+            vraw[i & 3] = raw;
+            if ((i & 3) == 3) {
+              const int ct = i >> 2;
+              const i32x8 vf = __builtin_bit_cast(
+                  i32x8, u32x8{vraw[0][0], vraw[0][1], vraw[1][0], vraw[1][1], vraw[2][0], vraw[2][1], vraw[3][0], vraw[3][1]});
+              o[t][ct] = mfma_f8(vf, pf[0], o[t][ct]);
+              o[t][ct] = mfma_f8(vf, pf[1], o[t][ct]);
+            }
+          });
     }
   }
 
   // ---- a7: epilogue (real rows only).
-  const int h = r16;
-  if (h < a.heads) {
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const bool any = l_run[j] > 0.f;
-      const float lse_v = any ? (m_run[j] + log2f(l_run[j])) * kLn2 : kNegInf;
-      const float sc = any ? a.out_scale / l_run[j] : 0.f;
-      const int64_t row = ((int64_t)b * a.num_q + j) * a.heads + h;
-      if constexpr (FINAL) {
-        uint16_t* dst = a.out + row * kValue + w * (kValue / kWaves) + 4 * g;
+  for (int t = 0; t < 2; ++t) {
+    const int row = 32 * t + r32;
+    const float l_run = t ? l_run1 : l_run0;
+    const float m_run = t ? m_run1 : m_run0;
+    if (row < R) {
+      const float sc = l_run > 0.f ? a.out_scale * (1.f / kPScale) / l_run : 0.f;
+      const int64_t orow = (int64_t)b * R + row;
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) {
-          bf16x4 ov;
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[j][ct][i] * sc);
-          *(bf16x4*)(dst + 16 * ct) = ov;
+        for (int q = 0; q < 4; ++q) {
+          const int col = 128 * w + 32 * ct + 8 * q + 4 * h;
+          const f32x4 v{o[t][ct][4 * q], o[t][ct][4 * q + 1], o[t][ct][4 * q + 2], o[t][ct][4 * q + 3]};
+          if constexpr (FINAL) {
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(v[i] * sc);
+            *(bf16x4*)(a.out + orow * kValue + col) = ov;
+          } else {
+            const int64_t prow = (int64_t)split * a.batch * R + orow;
+            *(f32x4*)(a.part_out + prow * kValue + col) = v * sc;
+          }
         }
-        if (w == 0 && g == 0) a.lse[row] = lse_v;
-      } else {
-        const int64_t prow = (int64_t)split * a.batch * a.num_q * a.heads + row;
-        float* dst = a.part_out + prow * kValue + w * (kValue / kWaves) + 4 * g;
-#pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) *(f32x4*)(dst + 16 * ct) = o[j][ct] * sc;
-        if (w == 0 && g == 0) a.part_lse[prow] = lse_v;
+      if (w == 0 && h == 0) {
+        const float lv = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
+        if constexpr (FINAL) a.lse[orow] = lv;
+        else a.part_lse[(int64_t)split * a.batch * R + orow] = lv;
       }
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int NQ, bool FP8>
-hipError_t launch_nq(const SplitArgs& a, bool final_out, hipStream_t stream) {
+template <int LAYOUT, bool FP8>
+hipError_t launch_layout(const SplitArgs& a, bool final_out, hipStream_t stream) {
   dim3 grid(a.num_splits, a.batch);
   if (final_out)
-    hipLaunchKernelGGL((split_kernel<NQ, FP8, true>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<LAYOUT, FP8, true>), grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((split_kernel<NQ, FP8, false>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<LAYOUT, FP8, false>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool FP8>
 hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) {
-  switch (a.num_q) {
-    case 1: return launch_nq<1, FP8>(a, final_out, stream);
-    case 2: return launch_nq<2, FP8>(a, final_out, stream);
-    case 3: return launch_nq<3, FP8>(a, final_out, stream);
-    default: return hipErrorInvalidValue;
+  const int rows = a.num_q * a.heads;
+  if (FP8 && rows > 32 && rows <= 64) {
+    dim3 grid(a.num_splits, a.batch);
+    if (final_out)
+      hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(split_kernel_f8x64<false>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
   }
+  if (rows <= 16) return launch_layout<kLayout16, FP8>(a, final_out, stream);
+  if (rows <= 48) return launch_layout<kLayout48, FP8>(a, final_out, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -176,8 +176,10 @@ def test_page_table_permutation_bitwise(gpu_lib):
     assert torch.equal(oa, ob) and torch.equal(la, lb)
 
 
-def test_head_padding_bitwise(gpu_lib):
-    """12 heads vs the same 12 + 4 zero-query heads: the real heads are bitwise equal."""
+def test_head_padding(gpu_lib):
+    """12 heads vs the same 12 + 4 zero-query heads: the real heads agree (rows are
+    packed token-major, so padding moves heads between MFMA tiles and only the
+    fp32 accumulation order may differ) and both match the oracle."""
     inp = make_inputs([100, 900], 3, 12, "fp8", seed=11, device="cuda")
     o12, l12 = run_verify(gpu_lib, inp, num_splits=3)
     q16 = torch.zeros((2, 3, 16, 576), dtype=torch.bfloat16, device="cuda")
@@ -185,7 +187,12 @@ def test_head_padding_bitwise(gpu_lib):
     o16, l16 = gpu_lib.verify(q16, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
                               inp.kv_scale, num_splits=3)
     torch.cuda.synchronize()
-    assert torch.equal(o16[:, :, :12], o12) and torch.equal(l16[:, :, :12], l12)
+    a, c = o16[:, :, :12].float(), o12.float()
+    assert (a - c).abs().max().item() <= 2.0 ** -7 * c.abs().max().item()
+    assert (l16[:, :, :12] - l12).abs().max().item() <= 1e-5
+    ro, rl, _ = oracle_out(inp)
+    compare(o16[:, :, :12].contiguous(), l16[:, :, :12].contiguous(), ro, rl, "H=16 padded")
+    compare(o12, l12, ro, rl, "H=12")
 
 
 def test_verify_equals_truncated_decodes(gpu_lib):
