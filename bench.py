@@ -33,6 +33,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 SPLIT_SRC = os.path.join(ROOT, "decode_attention_03_amd", "csrc", "mla_split.hip")
 
 
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -44,7 +48,14 @@ def _args():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+                    help="also run a plain 1 GiB elementwise copy (negation) for HBM counter "
+                         "calibration")
+    ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE", "FETCH", "WRITE", "MFMA"),
+                    help="no GPU: turn rocprofv3 output folders (kernel trace + stats, FETCH_SIZE, "
+                         "WRITE_SIZE, MFMA counters) of a --copy-calibration run into the "
+                         "summaries under profiles/")
+    ap.add_argument("--profile-tag", default="long_ctx_fp8_4x35500_q3_h12",
+                    help="workload tag in the summary file names")
     return ap.parse_args()
 
 
@@ -68,17 +79,199 @@ def _layers(cfg, device):
     return layers, c
 
 
-def _traffic(per_launch_alg_bytes):
+def _traffic(tag, num_splits):
     """HBM bytes per split-kernel launch from the committed counter summary, or
-    None when the summary is missing or was taken on another kernel source."""
-    path = os.path.join(PROFILES, "mla_split_c5_traffic.json")
+    None when the summary is missing or was taken on another kernel source or
+    split count."""
+    path = os.path.join(PROFILES, f"split_traffic__{tag}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     src_hash = hashlib.sha256(open(SPLIT_SRC, "rb").read()).hexdigest()
-    if rec.get("split_source_sha256") != src_hash:
+    if rec.get("split_source_sha256") != src_hash or rec.get("num_splits") != num_splits:
         return None
     return float(rec["hbm_bytes_per_dispatch"])
+
+
+def _read_csvs(folder, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
+        rows.extend(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {folder}")
+    return rows
+
+
+def _command_of(folder):
+    p = os.path.join(folder, "command.txt")
+    return open(p).read().strip() if os.path.exists(p) else "(command not recorded)"
+
+
+def _per_kernel(rows, pick):
+    """Mean counter values per dispatch of the kernels whose name satisfies pick."""
+    import collections
+    acc = collections.defaultdict(list)
+    for r in rows:
+        if pick(r["Kernel_Name"]):
+            acc[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def _is_split(name):
+    return "split_kernel" in name
+
+
+def _is_merge(name):
+    return "merge_kernel" in name
+
+
+def _is_calib(name):
+    return "neg_kernel" in name
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
+    """Writes profiles/kernel_stats__TAG.md, profiles/split_traffic__TAG.json/.md
+    from rocprofv3 output of `bench.py --copy-calibration` runs (CPU only)."""
+    import workloads
+    stats = _read_csvs(trace_dir, "kernel_stats.csv")
+    trace = _read_csvs(trace_dir, "kernel_trace.csv")
+    fetch = _read_csvs(fetch_dir, "counter_collection.csv")
+    write = _read_csvs(write_dir, "counter_collection.csv")
+    mfma = _read_csvs(mfma_dir, "counter_collection.csv")
+    os.makedirs(PROFILES, exist_ok=True)
+
+    # kernel time summary (rocprofv3 --stats), our kernels and the largest others
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    split_stat = [r for r in stats if _is_split(r["Name"])]
+    merge_stat = [r for r in stats if _is_merge(r["Name"])]
+    if not split_stat:
+        raise SystemExit("no split kernel in the kernel stats")
+    split_avg_us = float(split_stat[0]["AverageNs"]) / 1e3
+    # grid of the split kernel from the trace (workgroups = grid / 256 threads)
+    grids = sorted({int(r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"])
+                    for r in trace if _is_split(r["Kernel_Name"])})
+    lines = [f"# Kernel time: split + merge, workload {tag}", "",
+             "Command (from the repository root on the GPU host):", "", "```",
+             _command_of(trace_dir), "```", "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in stats[:8]:
+        name = r["Name"]
+        short = ("split: " if _is_split(name) else "merge: " if _is_merge(name) else "") + \
+            (name if len(name) < 90 else name[:87] + "...")
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    lines += ["", f"Split kernel grid sizes (threads): {grids}"]
+    open(os.path.join(PROFILES, f"kernel_stats__{tag}.md"), "w").write("\n".join(lines) + "\n")
+
+    # HBM bytes, calibrated on the 1 GiB negation (reads 1 GiB, writes 1 GiB)
+    cal_f = _per_kernel(fetch, _is_calib).get("FETCH_SIZE")
+    cal_w = _per_kernel(write, _is_calib).get("WRITE_SIZE")
+    spl_f = _per_kernel(fetch, _is_split)["FETCH_SIZE"]
+    spl_w = _per_kernel(write, _is_split)["WRITE_SIZE"]
+    mrg_f = _per_kernel(fetch, _is_merge).get("FETCH_SIZE", (0.0, 0))
+    mrg_w = _per_kernel(write, _is_merge).get("WRITE_SIZE", (0.0, 0))
+    if cal_f is None or cal_w is None:
+        raise SystemExit("calibration kernel (neg_kernel) missing from the counter runs")
+    gib = float(1 << 30)
+    ff = gib / (cal_f[0] * 1024.0)
+    fw = gib / (cal_w[0] * 1024.0)
+    split_bytes = spl_f[0] * 1024.0 * ff + spl_w[0] * 1024.0 * fw
+    merge_bytes = mrg_f[0] * 1024.0 * ff + mrg_w[0] * 1024.0 * fw
+
+    # algorithmic bytes per split launch of this workload (one layer)
+    cfg = tag_config(tag)
+    c = workloads.CONFIGS[cfg]
+    if "layers" in c:
+        inp = workloads.make_c5_layer(0, device="cpu", name=cfg)
+    else:
+        inp = workloads.make_config(cfg, device="cpu")
+    alg = workloads.algorithmic_bytes(inp.seq_lens.numpy(), inp.num_q, inp.heads, inp.kv_dtype)
+    S = _recorded_splits(trace_dir)
+
+    m = _per_kernel(mfma, _is_split)
+    mops8 = m.get("SQ_INSTS_VALU_MFMA_MOPS_F8", (0.0, 0))[0]
+    mops16 = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", (0.0, 0))[0]
+    busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", (0.0, 0))[0]
+    mfma_flops = (mops8 + mops16) * 512.0
+    rec = {
+        "kernel": split_stat[0]["Name"],
+        "workload": tag,
+        "config_key": cfg,
+        "num_splits": S,
+        "split_source_sha256": hashlib.sha256(open(SPLIT_SRC, "rb").read()).hexdigest(),
+        "split_avg_us": round(split_avg_us, 3),
+        "merge_avg_us": round(float(merge_stat[0]["AverageNs"]) / 1e3, 3) if merge_stat else None,
+        "fetch_kib_per_dispatch": round(spl_f[0], 1),
+        "write_kib_per_dispatch": round(spl_w[0], 1),
+        "dispatches_counted": spl_f[1],
+        "calibration": {"kernel": "torch.neg on 2^28 float32 (1 GiB read, 1 GiB written)",
+                        "fetch_kib": round(cal_f[0], 1), "write_kib": round(cal_w[0], 1),
+                        "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
+        "hbm_bytes_per_dispatch": round(split_bytes),
+        "algorithmic_bytes_per_dispatch": int(alg),
+        "traffic_over_algorithmic": round(split_bytes / alg, 4),
+        "achieved_gbs_from_profile": round(alg / (split_avg_us * 1e-6) / 1e9, 1),
+        "merge_hbm_bytes_per_dispatch": round(merge_bytes),
+        "mfma": {"executed_flops_per_dispatch": mfma_flops,
+                 "executed_tflops": round(mfma_flops / (split_avg_us * 1e-6) / 1e12, 2),
+                 "mfma_busy_cycles_per_dispatch": busy,
+                 "counters": "SQ_INSTS_VALU_MFMA_MOPS_F8/BF16 x 512 flops"},
+        "commands": [_command_of(d) for d in (fetch_dir, write_dir, mfma_dir)],
+    }
+    json.dump(rec, open(os.path.join(PROFILES, f"split_traffic__{tag}.json"), "w"), indent=1)
+    md = [f"# HBM traffic and MFMA work of the split kernel, workload {tag}", "",
+          "Counter passes (each its own run, from the repository root on the GPU host):", ""]
+    for cmd in rec["commands"]:
+        md += ["```", cmd, "```"]
+    md += ["", "Summarised with `python bench.py --summarize-profiles <trace> <fetch> <write> "
+           f"<mfma> --profile-tag {tag}`.", "",
+           "| quantity | value |", "|---|---|",
+           f"| split kernel average duration (kernel trace) | {split_avg_us:.2f} us |",
+           f"| split count | {S} |",
+           f"| FETCH_SIZE per dispatch | {spl_f[0]:.0f} KiB |",
+           f"| WRITE_SIZE per dispatch | {spl_w[0]:.0f} KiB |",
+           f"| calibration: 1 GiB negation reads / writes | {cal_f[0]:.0f} / {cal_w[0]:.0f} KiB "
+           f"(factors {ff:.3f} / {fw:.3f}) |",
+           f"| HBM bytes per split dispatch (calibrated) | {split_bytes / 1e6:.2f} MB |",
+           f"| algorithmic bytes per split dispatch | {alg / 1e6:.2f} MB |",
+           f"| traffic / algorithmic | {split_bytes / alg:.3f} |",
+           f"| achieved (algorithmic bytes / average duration) | "
+           f"{alg / (split_avg_us * 1e-6) / 1e9:.0f} GB/s = "
+           f"{alg / (split_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s |",
+           f"| HBM bytes per merge dispatch (calibrated) | {merge_bytes / 1e6:.2f} MB |",
+           f"| executed MFMA flops per split dispatch | {mfma_flops / 1e9:.2f} GFLOP "
+           f"({mfma_flops / (split_avg_us * 1e-6) / 1e12:.1f} TFLOP/s) |",
+           f"| MFMA busy cycles per split dispatch (sum over SIMDs) | {busy:.3g} |"]
+    open(os.path.join(PROFILES, f"split_traffic__{tag}.md"), "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+TAGS = {"long_ctx_fp8_4x35500_q3_h12": "c5", "long_ctx_fp8_4x142000_q3_h12": "c5b",
+        "fp8_verify_b64_q3_h12": "c4", "bf16_verify_b32_q3_h12": "c3",
+        "bf16_decode_b32_q1_h12": "c2", "tiny_decode_b1_l256": "c1"}
+
+
+def tag_config(tag):
+    return TAGS[tag]
+
+
+def config_tag(cfg):
+    return {v: k for k, v in TAGS.items()}[cfg]
+
+
+def _recorded_splits(folder):
+    """Split count from the bench JSON line saved beside the trace (bench.json)."""
+    p = os.path.join(folder, "bench.json")
+    if not os.path.exists(p):
+        return None
+    for ln in open(p):
+        if ln.startswith('{"metric"'):
+            return int(json.loads(ln)["config"]["num_splits"])
+    return None
 
 
 def _cpu_baseline(layers, budget_s):
@@ -120,6 +313,9 @@ def _cpu_baseline(layers, budget_s):
 
 def main():
     args = _args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.profile_tag)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
@@ -136,6 +332,7 @@ def main():
     torch.cuda.set_device(dev)
     layers, cfg = _layers(args.config, dev)
     n_layers = len(layers)
+    _log(f"{n_layers} layer input(s) of {args.config} resident on {dev}")
     hint = cfg["seq_hi"]
     first = layers[0]
     S = mla.num_splits(first.q, first.kv, first.page_table, args.num_splits, hint)
@@ -179,6 +376,7 @@ def main():
         step()
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    _log(f"eager: {eager_ms:.3f} ms per step")
 
     # Timed region: the step captured once as a HIP graph (the library neither
     # allocates nor synchronises, so it is capturable) and replayed K times;
@@ -204,6 +402,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
+    _log(f"graph replay: {ms_per_step:.3f} ms per step")
 
     alg = [workloads.algorithmic_bytes(l.seq_lens.cpu().numpy(), l.num_q, l.heads, l.kv_dtype)
            for l in layers]
@@ -232,7 +431,15 @@ def main():
     merge_us = timed(graphs["merge"], args.steps) if S > 1 else 0.0
     split_alg = float(np.mean(alg))     # one split launch processes one layer's batch
     achieved = split_alg / (split_us * 1e-6) / 1e9
-    traffic = _traffic(split_alg)
+    traffic = _traffic(config_tag(args.config), S)
+    # executed MFMA work of the split kernel (padded rows, two-term fp8 operands)
+    fp8 = first.kv_dtype == "fp8"
+    rows = first.num_q * first.heads
+    exec_rows = 64 if (fp8 and 32 < rows <= 64) else 16 if rows <= 16 else 48 if rows <= 48 else rows
+    terms = 2 if (fp8 and 32 < rows <= 64) else 1
+    positions = sum(int(l.seq_lens.sum().item()) for l in layers) / n_layers
+    mfma_exec = positions * exec_rows * terms * 2 * (576 + 512)
+    mfma_peak = 5000.0 if terms == 2 else 2500.0
 
     line = {
         "metric": METRIC,
@@ -245,7 +452,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if fp8 and terms == 2 else "bf16",
         "data": "synthetic",
         "us_per_layer_step": round(us_per_layer, 3),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
@@ -257,7 +464,8 @@ def main():
             "num_q_tokens": first.num_q,
             "heads": first.heads,
             "kv_dtype": "fp8_e4m3fn" if first.kv_dtype == "fp8" else "bf16",
-            "mfma_operands": "bf16, fp32 accumulate",
+            "mfma_operands": ("fp8 e4m3 (q and p each split into two fp8 terms), fp32 accumulate"
+                              if terms == 2 else "bf16, fp32 accumulate"),
             "num_splits": S,
             "algorithmic_bytes_per_step": int(bytes_per_step),
             "algorithmic_flops_per_step": int(sum(flops)),
@@ -277,15 +485,24 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
         },
+        "mfma_roofline": {
+            "kernel": "split_kernel",
+            "executed_tflops": round(mfma_exec / (split_us * 1e-6) / 1e12, 2),
+            "peak": mfma_peak,
+            "unit": "TFLOP/s",
+            "frac": round(mfma_exec / (split_us * 1e-6) / 1e12 / mfma_peak, 4),
+            "note": f"executed = {exec_rows} padded rows x {terms} operand term(s) x "
+                    "2 x (576 + 512) flops per position",
+        },
     }
+    _log(f"split {split_us:.2f} us, merge {merge_us:.2f} us per launch")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(layers, args.cpu_seconds)
     if args.copy_calibration:
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
     print(json.dumps(line), flush=True)
 
