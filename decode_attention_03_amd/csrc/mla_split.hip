@@ -82,11 +82,22 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 // traffic, then s_barrier.  (No memory fence: the direct-to-LDS loads are
 // waited for explicitly with vmcnt, so no blanket vmcnt(0) is wanted here.)
 __device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");   // compiler-only: no LDS access moves across
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m)); }
+// x combined with the value of lane l ^ 32 (a VALU lane swap, no LDS round trip)
+__device__ __forceinline__ float max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
 
 // 8 FP8 E4M3FN codes (two dwords) -> 8 bf16 (exact).
@@ -344,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       }
     }
     lds_barrier();  // tile `it` visible; every wave is done with tile it - 1
-    if (it + kNBuf - 1 < ntiles) issue_tile(it + kNBuf - 1);
+    issue_tile(it + kNBuf - 1);
 
     const int tpos0 = (p0 + it * TPG) * kPage;      // sequence position of tile slot 0
     const int tlim = (p1 - p0 - it * TPG) * kPage;  // tile slots inside the split
@@ -646,29 +657,195 @@ __device__ __forceinline__ void split4_fp8(float v0, float v1, float v2, float v
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(v2 - b23[0], v3 - b23[1], lo, true);
 }
 
+// Byte offset, from a lane's value base, of the 8 positions 8e..8e+7 (e < 4)
+// of column tile ct of the FP8 PV step (see the PV comment below).
+constexpr int pv_voff(int ct, int e) {
+  return (e >> 1) * KvGeom<true>::kPageB + 8 * (e & 1) * KvGeom<true>::kRowB +
+         16 * (4 * (ct >> 1) + 2 * ((ct ^ e) & 1));
+}
+
+// Four transposed FP8 LDS reads (column tile CT, positions 0..31 of the lane's
+// half) for the PV value operand.  Issued from inline assembly, which waits for
+// its own reads before it ends: the compiler would otherwise treat these reads
+// as possibly aliasing the in-flight direct-to-LDS copies of later tiles and
+// wait for all of them (vmcnt(0)), which defeats the copy pipeline.  The
+// copies of the tile being read were waited for explicitly before the barrier
+// that published it.
+// The two FP8 probability terms of one lane (32 bytes each, 64 * 80 bytes
+// apart), read the same way for the same reason.
+__device__ __forceinline__ void read_p_f8(uint32_t paddr, i32x8 (&pf)[2]) {
+  u32x4 a0, a1, b0, b1;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:16\n\t"
+      "ds_read_b128 %2, %4 offset:5120\n\t"
+      "ds_read_b128 %3, %4 offset:5136\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+      : "v"(paddr));
+  pf[0] = __builtin_bit_cast(i32x8, u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+  pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
+}
+
+// Key operand of one k-step: 16 bytes at each of two lane addresses (chunks
+// 4ks + 2h and 4ks + 2h + 1 of the lane's position row), read the same way.
+template <int OFF>
+__device__ __forceinline__ i32x8 read_k_f8(uint32_t a0, uint32_t a1) {
+  u32x4 v0, v1;
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%4\n\t"
+      "ds_read_b128 %1, %3 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1)
+      : "v"(a0), "v"(a1), "i"(OFF));
+  return __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+}
+
+// All LDS operands of one PV step in one block: the value operand of column
+// tiles 0 and 1 (four transposed reads each, at pv_voff(ct, e)) and the two
+// probability terms of row tiles 0 and 1 (rows 32t + r32: 80 * 32 bytes apart).
+static_assert(pv_voff(0, 0) == 0 && pv_voff(0, 1) == 4640 && pv_voff(0, 2) == 9216 &&
+              pv_voff(0, 3) == 13856 && pv_voff(1, 0) == 32 && pv_voff(1, 1) == 4608 &&
+              pv_voff(1, 2) == 9248 && pv_voff(1, 3) == 13824, "offsets in read_pv_f8");
+__device__ __forceinline__ void read_pv_f8(uint32_t vaddr, uint32_t paddr, u32x2 (&v)[8], u32x4 (&p)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %16\n\t"
+      "ds_read_b64_tr_b8 %1, %16 offset:4640\n\t"
+      "ds_read_b64_tr_b8 %2, %16 offset:9216\n\t"
+      "ds_read_b64_tr_b8 %3, %16 offset:13856\n\t"
+      "ds_read_b64_tr_b8 %4, %16 offset:32\n\t"
+      "ds_read_b64_tr_b8 %5, %16 offset:4608\n\t"
+      "ds_read_b64_tr_b8 %6, %16 offset:9248\n\t"
+      "ds_read_b64_tr_b8 %7, %16 offset:13824\n\t"
+      "ds_read_b128 %8, %17\n\t"
+      "ds_read_b128 %9, %17 offset:16\n\t"
+      "ds_read_b128 %10, %17 offset:5120\n\t"
+      "ds_read_b128 %11, %17 offset:5136\n\t"
+      "ds_read_b128 %12, %17 offset:2560\n\t"
+      "ds_read_b128 %13, %17 offset:2576\n\t"
+      "ds_read_b128 %14, %17 offset:7680\n\t"
+      "ds_read_b128 %15, %17 offset:7696\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+        "=&v"(v[7]), "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3]), "=&v"(p[4]), "=&v"(p[5]),
+        "=&v"(p[6]), "=&v"(p[7])
+      : "v"(vaddr), "v"(paddr));
+}
+
+template <int CT>
+__device__ __forceinline__ void read_v_f8(uint32_t vaddr, u32x2 (&r)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %4 offset:%5\n\t"
+      "ds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b8 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b8 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(vaddr), "i"(pv_voff(CT, 0)), "i"(pv_voff(CT, 1)), "i"(pv_voff(CT, 2)),
+        "i"(pv_voff(CT, 3)));
+}
+
+constexpr int kF8Waves = 8;
+constexpr int kF8Threads = kF8Waves * 64;
+
+// Value operand of one PV step: column tiles 0..3 (128 columns) x positions
+// 32h + 0..31, sixteen transposed reads at the offsets pv_voff(ct, e).
+static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 9280 &&
+              pv_voff(2, 3) == 13920 && pv_voff(3, 0) == 96 && pv_voff(3, 1) == 4672 &&
+              pv_voff(3, 2) == 9312 && pv_voff(3, 3) == 13888, "offsets in read_v128_f8");
+__device__ __forceinline__ void read_v128_f8(uint32_t vaddr, u32x2 (&v)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %16\n\t"
+      "ds_read_b64_tr_b8 %1, %16 offset:4640\n\t"
+      "ds_read_b64_tr_b8 %2, %16 offset:9216\n\t"
+      "ds_read_b64_tr_b8 %3, %16 offset:13856\n\t"
+      "ds_read_b64_tr_b8 %4, %16 offset:32\n\t"
+      "ds_read_b64_tr_b8 %5, %16 offset:4608\n\t"
+      "ds_read_b64_tr_b8 %6, %16 offset:9248\n\t"
+      "ds_read_b64_tr_b8 %7, %16 offset:13824\n\t"
+      "ds_read_b64_tr_b8 %8, %16 offset:64\n\t"
+      "ds_read_b64_tr_b8 %9, %16 offset:4704\n\t"
+      "ds_read_b64_tr_b8 %10, %16 offset:9280\n\t"
+      "ds_read_b64_tr_b8 %11, %16 offset:13920\n\t"
+      "ds_read_b64_tr_b8 %12, %16 offset:96\n\t"
+      "ds_read_b64_tr_b8 %13, %16 offset:4672\n\t"
+      "ds_read_b64_tr_b8 %14, %16 offset:9312\n\t"
+      "ds_read_b64_tr_b8 %15, %16 offset:13888\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+        "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
+        "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(vaddr));
+}
+
+// The two probability terms (32 bytes each) of one lane's row, 2560 bytes apart.
+__device__ __forceinline__ void read_p32_f8(uint32_t paddr, i32x8 (&pf)[2]) {
+  u32x4 a0, a1, b0, b1;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:16\n\t"
+      "ds_read_b128 %2, %4 offset:2560\n\t"
+      "ds_read_b128 %3, %4 offset:2576\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+      : "v"(paddr));
+  pf[0] = __builtin_bit_cast(i32x8, u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+  pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
+}
+
+// Eight waves in two groups of four; group g owns query rows 32g..32g+31 and
+// waves 4g..4g+3, and SIMD k runs wave k of group 0 and wave k of group 1.
+// Within a group, wave v = w & 3:
+//   QK:  position half sp = v & 1 of the 64-position tile and dimension half
+//        dh = v >> 1 (k-steps 0..4 or 5..8 of 64 dims): 80 registers of query
+//        fragments.  Partners v and v ^ 2 add their partial scores through
+//        LDS; the dh = 1 wave reads its key rows rotated by 16 positions, so
+//        both keep accumulator elements 0..7 (positions 16dh + 0..15 of the
+//        half) and send elements 8..15.
+//   PV:  output columns 128v..128v+127 for the group's 32 rows.
+// The groups run one phase apart (each phase ends with a workgroup barrier):
+//   phase E(i): group 0: PV(i-1), QK(i)   | group 1: softmax(i-1)
+//   phase O(i): group 0: softmax(i)       | group 1: PV(i-1), QK(i)
+// so on every SIMD one wave issues MFMAs while the other does the softmax
+// arithmetic.  QK(i) also reads the tile's value fragments into registers,
+// so a tile is only read in E(i) and O(i): buffer (i + 2) % 3 can be refilled
+// at the start of E(i), two tiles ahead.
+// Probabilities use a per-row reference maximum that moves only when a tile
+// maximum exceeds it by more than 2^kSlack; the check runs at the start of
+// the phase after each softmax, on data every wave reads, so the rare
+// recomputation (and its barriers) is taken by all waves together.
 template <bool FINAL>
-__global__ __launch_bounds__(kThreads, 1) void split_kernel_f8x64(SplitArgs a) {
+__global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using G = KvGeom<true>;
   constexpr int kNBuf = 3;
   constexpr int kTileB = kTilePages * G::kPageB;          // 36,864
-  constexpr int kWaveLoads = G::kPageB / 1024;            // 9: wave w copies page w
+  constexpr int kWaveLoads = G::kPageB / 1024;            // 9 wave-wide 1 KiB copies per page
   constexpr int kPRB = kTilePos + 16;                     // bytes per FP8 probability row (+skew)
-  constexpr float kSlack = 4.f;                           // log2 headroom of the lazy rescale
-  constexpr float kPScale = 16.f;                         // 2^(8 - kSlack)
+  constexpr int kPTerm = 32 * kPRB;                       // 2560: second probability term
+  constexpr float kSlack = 4.f;                           // p * 2^kPShift <= 256
+  constexpr float kPShift = 4.f;
+  static_assert(kPTerm == 2560, "read_p32_f8 assumes 2560 bytes between the terms");
 
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2 * 64 * kPRB];  // [term][row][position]
-  __shared__ float red_max[kWaves][32];
-  __shared__ float red_sum[kWaves][32];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][2 * kPTerm];   // [group][term][row][position]
+  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][2][64];    // partial scores for the partner
+  __shared__ float red_max[kF8Waves][32];
+  __shared__ float red_sum[kF8Waves][32];
+  __shared__ float qmax[kF8Waves][32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int h = lane >> 5;
-  const int rt = w >> 1;         // row tile: rows 32*rt .. 32*rt + 31
-  const int sp = w & 1;          // tile positions 32*sp .. 32*sp + 31
+  const int g16 = lane >> 4;
+  const int grp = w >> 2;
+  const int v4 = w & 3;
+  const int sp = v4 & 1;
+  const int dh = v4 >> 1;
+  const int ks0 = dh ? 5 : 0;
+  const int nks = dh ? 4 : 5;
   const int split = blockIdx.x;
   const int b = blockIdx.y;
   const int H = a.heads;
@@ -679,73 +856,86 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel_f8x64(SplitArgs a) {
   const int p0 = (int)(((int64_t)split * P) / a.num_splits);
   const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
   const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
-  // read-only page table through the constant address space: uniform
-  // indices become scalar loads, which do not count against vmcnt
-  const __attribute__((address_space(4))) int32_t* pt_row =
-      (const __attribute__((address_space(4))) int32_t*)(a.page_table + (int64_t)b * a.max_blocks);
 
-  const int myrow = 32 * rt + r32;
+  const int myrow = 32 * grp + r32;
   const int lim = L - a.num_q + myrow / H + 1;   // visible: position < lim
 
-  float m_run0 = kNegInf, l_run0 = 0.f, m_run1 = kNegInf, l_run1 = 0.f;
-  f32x16 o[2][4];
+  // ---- a2: copies.  Tile T goes to LDS buffer T % 3.  Waves 0..3 copy the
+  // tiles with T even and waves 4..7 those with T odd, wave w copying page w % 4
+  // (nine wave-wide one-KiB loads from one buffer descriptor), so each wave has
+  // at most one page in flight and two tiles are in flight per workgroup.  A
+  // page outside the split, or the positions past seq_len in the last page, lie
+  // outside the buffer range and are written to LDS as zeros by the copy itself.
+  const int cpar = w >> 2;
+  uint32_t voff[kWaveLoads];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) o[t][c] = f32x16{};
-
-  // ---- a2: tile T -> LDS buffer T % 3; wave w copies page w of the tile.
-  auto issue_tile = [&](int T) {
-    uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + w * G::kPageB;
-    const int page = p0 + T * kTilePages + w;
-    if (page < p1) {
-      const int blk = __builtin_amdgcn_readfirstlane(pt_row[page]);
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.kv + (int64_t)blk * G::kPageB), 0, G::kPageB, kBufferRsrcWord3);
-      // recompute the per-lane offsets at every copy instead of keeping nine
-      // loop-invariant registers alive across the whole loop
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-#pragma unroll
-      for (int c = 0; c < kWaveLoads; ++c) {
-        const uint32_t slot = 64 * c + ln;
-        const uint32_t row = slot / G::kChunksPerRow;
-        const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16,
-                                                 row * G::kRowB + x * 16, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < kWaveLoads; ++c)
-        *(u32x4*)(dst + 1024 * c + 16 * lane) = u32x4{0, 0, 0, 0};
-    }
+  for (int c = 0; c < kWaveLoads; ++c) {
+    const uint32_t slot = 64 * c + lane;
+    const uint32_t row = slot / G::kChunksPerRow;
+    const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
+    voff[c] = row * G::kRowB + x * 16;
+  }
+  // Page-table entry of the page copied from tile T, loaded two tiles ahead
+  // with a vector load (entries past the sequence are clamped to its last page
+  // and not used).
+  const int32_t* pt_b = a.page_table + (int64_t)b * a.max_blocks;
+  const int plast = max(P - 1, 0);
+  auto pt_load = [&](int T) -> int {
+    return pt_b[min(p0 + T * kTilePages + v4, plast)];
   };
-  auto has_page = [&](int T) { return p0 + T * kTilePages + w < p1; };
-
+  auto issue_tile = [&](int T, int ptv) {
+    const int gp = p0 + T * kTilePages + v4;
+    const int blk = __builtin_amdgcn_readfirstlane(ptv);
+    const int bytes = gp < p1 ? min(kPage, L - gp * kPage) * G::kRowB : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB), 0, bytes, kBufferRsrcWord3);
+    uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + v4 * G::kPageB;
 #pragma unroll
-  for (int T = 0; T < kNBuf - 1; ++T)
-    if (T < ntiles) issue_tile(T);
+    for (int c = 0; c < kWaveLoads; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16, voff[c], 0, 0, 0);
+  };
+  // Vector-memory order of a wave: PT(T + 2), copies(T), then nothing until
+  // copies(T) are waited for (vmcnt(0)) at the start of E(T).
 
-  // The first copies are in flight while the query is prepared.
-  // ---- query: q * 2^e = q1 + q2 (FP8), dims 64ks + 32h + j of row `myrow`.
-  i32x8 q1[9], q2[9];
+  // ---- query: q * 2^e = q1 + q2 (FP8), dims 64(ks0 + ks) + 32h + j of row `myrow`.
+  // The query loads go out before the first copies (vmcnt counts in issue
+  // order), so waiting for them leaves the copies in flight.
+  i32x8 q1[5], q2[5];
   float q_unscale;
+  int ptc;   // page-table entries of the next tile to copy
   {
     const bool real = myrow < R && ntiles > 0;   // empty splits skip the query work
     const uint16_t* qp = a.q + ((int64_t)b * R + (real ? myrow : 0)) * kLatent + 32 * h;
+    const uint32_t keep = real ? 0xFFFFFFFFu : 0u;
+    const int pt0 = pt_load(cpar);
+    ptc = pt_load(cpar + 2);
+    u32x4 qv[5][4];
+#pragma unroll
+    for (int ks = 0; ks < 5; ++ks) {
+      // the fifth step of dh = 1 does not exist: reload step 8 and drop it below
+      const int kk = min(ks0 + ks, 8);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qv[ks][c] = *(const u32x4*)(qp + 64 * kk + 8 * c);
+    }
+    asm volatile("" ::: "memory");   // keep the query loads ahead of the copies
+    issue_tile(cpar, pt0);
+    __builtin_amdgcn_sched_barrier(0);   // and the copies ahead of the query arithmetic
     float mx = 0.f;
-    if (real) {
 #pragma unroll
-      for (int ks = 0; ks < 9; ++ks)
+    for (int ks = 0; ks < 5; ++ks) {
+      const uint32_t kp = (ks < nks) ? keep : 0u;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 v = *(const u32x4*)(qp + 64 * ks + 8 * c);
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[k])), fabsf(bf16_hi(v[k]))));
+        for (int k = 0; k < 4; ++k) {
+          qv[ks][c][k] &= kp;
+          mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(qv[ks][c][k])), fabsf(bf16_hi(qv[ks][c][k]))));
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));            // the two lanes holding this row
+    mx = max32(mx);                                 // the two lanes holding this row
+    if (h == 0) qmax[w][r32] = mx;
+    lds_barrier();
+    mx = fmaxf(qmax[w][r32], qmax[w ^ 2][r32]);     // the other half of the dims
     int e = 0;
     if (mx > 0.f) {
       const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126;  // mx = m * 2^ex, m in [0.5, 1)
@@ -754,11 +944,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel_f8x64(SplitArgs a) {
     const float sc = pow2f(e);
     q_unscale = pow2f(-e);
 #pragma unroll
-    for (int ks = 0; ks < 9; ++ks) {
+    for (int ks = 0; ks < 5; ++ks) {
       i32x8 hi8, lo8;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const u32x4 v = real ? *(const u32x4*)(qp + 64 * ks + 8 * c) : u32x4{0, 0, 0, 0};
+        const u32x4 v = qv[ks][c];
         int hh, ll;
         split4_fp8(bf16_lo(v[0]) * sc, bf16_hi(v[0]) * sc, bf16_lo(v[1]) * sc, bf16_hi(v[1]) * sc, hh, ll);
         hi8[2 * c] = hh;
@@ -771,192 +961,237 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel_f8x64(SplitArgs a) {
       q2[ks] = lo8;
     }
   }
-
-
+  // scale of this lane's scores (row `myrow`) into the log2 domain
   const float cs = a.score_scale_log2 * q_unscale;
 
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles && has_page(it + 1))
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    uint8_t* tile = kv_lds + (it % kNBuf) * kTileB;
+  // Reference maxima of rows r32 of group 0 and group 1 (every wave tracks
+  // both, from the same LDS data), the row sum of this wave's row, and the
+  // output of this wave's 128 columns x the group's 32 rows.
+  float mref0 = kNegInf, mref1 = kNegInf;
+  float l_run = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = f32x16{};
+  i32x8 vfr[4];     // value fragments of the group's next PV
+  float x[8];       // scores of this wave's last softmax (kept for a recomputation)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = kNegInf;
+
+  const int prow = r32 & 15;
+  const int kpage = 2 * sp + ((r32 >> 4) ^ dh);
+  const int sl = lane & 15;
+  const int vbase = 2 * h * G::kPageB + (sl >> 1) * G::kRowB + 16 * (8 * v4 + ((g16 ^ (sl >> 3)) & 1)) + 8 * (sl & 1);
+  const int pbase = r32 * kPRB + 32 * sp + 16 * dh + 4 * h;
+  uint8_t* const pg_lds = p_lds[grp];
+
+  // ---- a4: partial S^T over this wave's k-steps, then the value fragments.
+  auto qk = [&](int T) {
+    const uint8_t* tile = kv_lds + (T % kNBuf) * kTileB;
+    f32x16 s = f32x16{};
+    const uint32_t kb0 = (uint32_t)(uintptr_t)LDS_PTR(
+        const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h, 0) + 64 * ks0);
+    const uint32_t kb1 = (uint32_t)(uintptr_t)LDS_PTR(
+        const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h + 1, 0) + 64 * ks0);
+    // the reads of step ks + 1 run while the two MFMAs of step ks execute
+    i32x8 kc = read_k_f8<0>(kb0, kb1);
+    s = mfma_f8(kc, q1[0], s);
+    s = mfma_f8(kc, q2[0], s);
+    __builtin_amdgcn_sched_barrier(0);
+    kc = read_k_f8<64>(kb0, kb1);
+    s = mfma_f8(kc, q1[1], s);
+    s = mfma_f8(kc, q2[1], s);
+    __builtin_amdgcn_sched_barrier(0);
+    kc = read_k_f8<128>(kb0, kb1);
+    s = mfma_f8(kc, q1[2], s);
+    s = mfma_f8(kc, q2[2], s);
+    __builtin_amdgcn_sched_barrier(0);
+    kc = read_k_f8<192>(kb0, kb1);
+    s = mfma_f8(kc, q1[3], s);
+    s = mfma_f8(kc, q2[3], s);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!dh) {
+      kc = read_k_f8<256>(kb0, kb1);
+      s = mfma_f8(kc, q1[4], s);
+      s = mfma_f8(kc, q2[4], s);
+    }
+    // elements 8..15 belong to the partner wave; elements 0..7 stay for softmax
+    xbuf[w][0][lane] = f32x4{s[8], s[9], s[10], s[11]};
+    xbuf[w][1][lane] = f32x4{s[12], s[13], s[14], s[15]};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = s[k];
+    // value operand for the PV of this tile (read now: the tile is not read
+    // after this phase).  Column tile ct, positions 32h + 8e .. +7: source lane
+    // sl of a 16-lane group reads position 32h + 8e + sl/2, i.e. page 2h + e/2,
+    // row 8(e%2) + sl/2, byte half sl%2 of chunk 8v + 2ct + (g16%2),
+    // XOR-swizzled by (row/4)%4 = sl/8 + 2(e%2); vbase is the lane part of that
+    // address and pv_voff(ct, e) the rest.
     {
-      const int page = p0 + it * kTilePages + w;
-      const int valid = L - page * kPage;
-      if (page < p1 && valid < kPage) {
-        uint8_t* pg = tile + w * G::kPageB;
-        for (int c = lane; c < (kPage - valid) * G::kChunksPerRow; c += 64)
-          *(u32x4*)(pg + (valid * G::kChunksPerRow + c) * 16) = u32x4{0, 0, 0, 0};
+      u32x2 vr[16];
+      read_v128_f8((uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + vbase), vr);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        vfr[ct] = __builtin_bit_cast(i32x8, u32x8{vr[4 * ct][0], vr[4 * ct][1], vr[4 * ct + 1][0],
+                                                  vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
+                                                  vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
+    }
+  };
+
+  // probabilities p * 2^kPShift against the reference maximum, as two FP8 terms
+  auto probs = [&](float m) {
+    const float c0 = kPShift - (m == kNegInf ? 0.f : m);
+    float ps = 0.f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float p4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p4[i] = __builtin_amdgcn_exp2f(x[4 * q + i] + c0);
+        ps += p4[i];
+      }
+      int hi, lo;
+      split4_fp8(p4[0], p4[1], p4[2], p4[3], hi, lo);
+      *(int*)(pg_lds + pbase + 8 * q) = hi;
+      *(int*)(pg_lds + kPTerm + pbase + 8 * q) = lo;
+    }
+    ps = sum32(ps);
+    if (h == 0) red_sum[w][r32] = ps;
+  };
+
+  // ---- a5: partner's partial scores added, scale to log2 units, mask (edge
+  // tiles only), tile maxima, probabilities.  Element k of x is position
+  // 32sp + 16dh + 8(k/4) + 4h + k%4 of the tile.
+  auto softmax = [&](int T) {
+    {
+      const f32x4 u0 = xbuf[w ^ 2][0][lane];
+      const f32x4 u1 = xbuf[w ^ 2][1][lane];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[k] += u0[k];
+        x[4 + k] += u1[k];
       }
     }
-    lds_barrier();  // tile `it` visible; every wave is done with tile it - 1
-    if (it + kNBuf - 1 < ntiles) issue_tile(it + kNBuf - 1);
-
-    const int tpos0 = (p0 + it * kTilePages) * kPage;
-    const int tlim = (p1 - p0 - it * kTilePages) * kPage;
-
-    // ---- a4: S^T for positions 32sp + (0..31) against row tile rt.
-    f32x16 s = f32x16{};
-    {
-      // The swizzle XORs only the low two bits of the chunk index, so chunk
-      // 4ks + c (c < 4) sits at 64ks bytes past chunk c: two lane bases plus
-      // immediate offsets address every k-step.
-      const int prow = r32 & 15;
-      const uint8_t* kb0 = tile + (2 * sp + (r32 >> 4)) * G::kPageB + G::off(prow, 2 * h, 0);
-      const uint8_t* kb1 = tile + (2 * sp + (r32 >> 4)) * G::kPageB + G::off(prow, 2 * h + 1, 0);
-      pipelined<9, 1, i32x8>(
-          [&](int ks) {
-            const u32x4 v0 = *(const u32x4*)(kb0 + 64 * ks);
-            const u32x4 v1 = *(const u32x4*)(kb1 + 64 * ks);
-            return __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-          },
-          [&](int ks, i32x8 kf) {
-            s = mfma_f8(kf, q1[ks], s);
-            s = mfma_f8(kf, q2[ks], s);
-          });
-    }
-
-    // ---- a5: mask (edge tiles only), scale, row maxima (two 32-position halves per row tile).
+    const int tpos0 = (p0 + T * kTilePages) * kPage;
+    const int tlim = (p1 - p0 - T * kTilePages) * kPage;
     float mx = kNegInf;
-    if (tlim >= kTilePos && tpos0 + kTilePos <= L - a.num_q + 1) {  // every row sees the whole tile
+    if (tlim >= kTilePos && tpos0 + kTilePos <= L - a.num_q + 1) {   // every row sees the whole tile
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] *= cs;
-        mx = fmaxf(mx, s[i]);
+      for (int k = 0; k < 8; ++k) {
+        x[k] *= cs;
+        mx = fmaxf(mx, x[k]);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tq = 32 * sp + 8 * (i >> 2) + 4 * h + (i & 3);
+      for (int k = 0; k < 8; ++k) {
+        const int tq = 32 * sp + 16 * dh + 8 * (k >> 2) + 4 * h + (k & 3);
         const bool ok = tq < tlim && tpos0 + tq < lim;
-        s[i] = ok ? s[i] * cs : kNegInf;
-        mx = fmaxf(mx, s[i]);
+        x[k] = ok ? x[k] * cs : kNegInf;
+        mx = fmaxf(mx, x[k]);
       }
     }
-    mx = xor_max(mx, 32);
+    mx = max32(mx);
     if (h == 0) red_max[w][r32] = mx;
-    lds_barrier();
+    probs(grp ? mref1 : mref0);
+  };
 
-    // Lazy rescale: a row's reference maximum moves only when the tile maximum
-    // exceeds it by more than 2^kSlack; probabilities are then at most 2^kSlack
-    // and their FP8 split stays in range (p * 2^(8 - kSlack) <= 256).
-    const float mt0 = fmaxf(red_max[0][r32], red_max[1][r32]);
-    const float mt1 = fmaxf(red_max[2][r32], red_max[3][r32]);
-    const float mn0 = (mt0 > m_run0 + kSlack) ? mt0 : m_run0;
-    const float mn1 = (mt1 > m_run1 + kSlack) ? mt1 : m_run1;
-    const float alpha0 = (mn0 == m_run0) ? 1.f : __builtin_amdgcn_exp2f(m_run0 - mn0);
-    const float alpha1 = (mn1 == m_run1) ? 1.f : __builtin_amdgcn_exp2f(m_run1 - mn1);
-    m_run0 = mn0;
-    m_run1 = mn1;
-    {
-      const float mm = rt ? mn1 : mn0;
-      float ps = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float p4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = s[4 * q + i];
-          p4[i] = (v == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(v - mm);
-          ps += p4[i];
-        }
-        int hi, lo;
-        split4_fp8(p4[0] * kPScale, p4[1] * kPScale, p4[2] * kPScale, p4[3] * kPScale, hi, lo);
-        const int off = myrow * kPRB + 32 * sp + 8 * q + 4 * h;
-        *(int*)(p_lds + off) = hi;
-        *(int*)(p_lds + 64 * kPRB + off) = lo;
+  // Start of the phase after group gx's softmax: move gx's reference maxima
+  // where a tile maximum passed them by more than 2^kSlack, and in that (rare,
+  // workgroup-uniform) case let gx recompute its probabilities.
+  auto check = [&](int gx) {
+    const float nm = fmaxf(fmaxf(red_max[4 * gx][r32], red_max[4 * gx + 1][r32]),
+                           fmaxf(red_max[4 * gx + 2][r32], red_max[4 * gx + 3][r32]));
+    const float mo = gx ? mref1 : mref0;
+    const bool ov = nm > mo + kSlack;
+    if (__any(ov)) {
+      const float mn = ov ? nm : mo;
+      if (grp == gx) {
+        const float alpha = ov ? __builtin_amdgcn_exp2f(mo - mn) : 1.f;
+        l_run *= alpha;
+        o[0] *= alpha;
+        o[1] *= alpha;
+        o[2] *= alpha;
+        o[3] *= alpha;
       }
-      ps = xor_sum(ps, 32);
-      if (h == 0) red_sum[w][r32] = ps;
+      if (gx) mref1 = mn;
+      else mref0 = mn;
+      lds_barrier();   // every wave has read the maxima (and the first sums)
+      if (grp == gx) probs(mn);
+      lds_barrier();
     }
+  };
+
+  // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127.
+  auto pv = [&]() {
+    l_run += (red_sum[4 * grp][r32] + red_sum[4 * grp + 1][r32]) +
+             (red_sum[4 * grp + 2][r32] + red_sum[4 * grp + 3][r32]);
+    i32x8 pf[2];
+    read_p32_f8((uint32_t)(uintptr_t)LDS_PTR(const uint8_t, pg_lds + r32 * kPRB + 32 * h), pf);
+    // written out: a rolled loop here makes the compiler rotate the four
+    // accumulators through one register window with moves
+    o[0] = mfma_f8(vfr[0], pf[0], o[0]);
+    o[1] = mfma_f8(vfr[1], pf[0], o[1]);
+    o[2] = mfma_f8(vfr[2], pf[0], o[2]);
+    o[3] = mfma_f8(vfr[3], pf[0], o[3]);
+    o[0] = mfma_f8(vfr[0], pf[1], o[0]);
+    o[1] = mfma_f8(vfr[1], pf[1], o[1]);
+    o[2] = mfma_f8(vfr[2], pf[1], o[2]);
+    o[3] = mfma_f8(vfr[3], pf[1], o[3]);
+  };
+
+  // Half-steps hs = 0, 1, ...: E(i) = 2i, O(i) = 2i + 1.  Group g's own step
+  // count is hs - g: even -> MFMA role (PV of tile T - 1, QK of tile T,
+  // T = (hs - g) / 2), odd -> softmax of tile T = (hs - g - 1) / 2.  At each
+  // half-step the group that ran its softmax in the previous one (g = hs % 2)
+  // is checked first.
+  for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
+    const bool mine = (hs & 1) == 0 && ((hs >> 1) & 1) == cpar;   // this wave copied tile hs / 2
+    if (mine) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
-
-    l_run0 = l_run0 * alpha0 + (red_sum[0][r32] + red_sum[1][r32]);
-    l_run1 = l_run1 * alpha1 + (red_sum[2][r32] + red_sum[3][r32]);
-    if (__any(alpha0 != 1.f || alpha1 != 1.f)) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        o[0][c] *= alpha0;
-        o[1][c] *= alpha1;
-      }
+    if (mine) {
+      const int it = hs >> 1;
+      const int ptn = pt_load(it + 4);
+      asm volatile("" ::: "memory");   // keep PT(it + 4) ahead of the copies
+      issue_tile(it + 2, ptc);
+      ptc = ptn;
     }
-
-    // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128w .. 128w + 127.
-    // One row tile at a time (the value operand is read twice) keeps the
-    // probability operands to 16 registers.
-    const int g = lane >> 4;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      i32x8 pf[2];
-#pragma unroll
-      for (int term = 0; term < 2; ++term) {
-        const uint8_t* pr = p_lds + term * 64 * kPRB + (32 * t + r32) * kPRB + 32 * h;
-        const u32x4 v0 = *(const u32x4*)pr;
-        const u32x4 v1 = *(const u32x4*)(pr + 16);
-        pf[term] = __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-      }
-      // step i: column tile ct = i/4, positions 32h + 8e .. +7 with e = i%4 (one
-      // transposed read each).  Source lane s of a 16-lane group reads position
-      // 32h + 8e + s/2, i.e. page 2h + e/2, row 8(e%2) + s/2, byte half s%2 of
-      // chunk 8w + 2ct + (g%2), XOR-swizzled by (row/4)%4 = s/8 + 2(e%2).  Split
-      // into a lane part and a constant part:
-      //   bits 0 of chunk: (g ^ s/8) % 2          (lane)
-      //   bit 1 of chunk:  (ct ^ e) % 2           (constant)
-      //   higher bits:     8w + 4(ct/2)            (constant per wave)
-      u32x2 vraw[4];
-      const int sl = lane & 15;
-      const uint8_t* vb = tile + 2 * h * G::kPageB + (sl >> 1) * G::kRowB +
-                          16 * (8 * w + ((g ^ (sl >> 3)) & 1)) + 8 * (sl & 1);
-      pipelined<16, 4, u32x2>(
-          [&](int i) {
-            const int e = i & 3, ct = i >> 2;
-            const int cst = (e >> 1) * G::kPageB + 8 * (e & 1) * G::kRowB + 16 * (4 * (ct >> 1) + 2 * ((ct ^ e) & 1));
-            return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vb + cst)));
-          },
-          [&](int i, u32x2 raw) {
-            vraw[i & 3] = raw;
-            if ((i & 3) == 3) {
-              const int ct = i >> 2;
-              const i32x8 vf = __builtin_bit_cast(
-                  i32x8, u32x8{vraw[0][0], vraw[0][1], vraw[1][0], vraw[1][1], vraw[2][0], vraw[2][1], vraw[3][0], vraw[3][1]});
-              o[t][ct] = mfma_f8(vf, pf[0], o[t][ct]);
-              o[t][ct] = mfma_f8(vf, pf[1], o[t][ct]);
-            }
-          });
+    if (hs >= 2) check(hs & 1);
+    const int st = hs - grp;
+    if (st >= 0 && (st & 1) == 0) {
+      const int T = st >> 1;
+      if (T >= 1) pv();
+      if (T < ntiles) qk(T);
+    } else if (st >= 1) {
+      const int T = (st - 1) >> 1;
+      if (T < ntiles) softmax(T);
     }
   }
 
-  // ---- a7: epilogue (real rows only).
+  // no copy may still be writing this workgroup's LDS when it ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // ---- a7: epilogue (real rows only).  O and l both carry the 2^kPShift factor.
+  if (myrow < R) {
+    const float sc = l_run > 0.f ? a.out_scale / l_run : 0.f;
+    const int64_t orow = (int64_t)b * R + myrow;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = 32 * t + r32;
-    const float l_run = t ? l_run1 : l_run0;
-    const float m_run = t ? m_run1 : m_run0;
-    if (row < R) {
-      const float sc = l_run > 0.f ? a.out_scale * (1.f / kPScale) / l_run : 0.f;
-      const int64_t orow = (int64_t)b * R + row;
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int q = 0; q < 4; ++q) {
+        const int col = 128 * v4 + 32 * ct + 8 * q + 4 * h;
+        const f32x4 v{o[ct][4 * q], o[ct][4 * q + 1], o[ct][4 * q + 2], o[ct][4 * q + 3]};
+        if constexpr (FINAL) {
+          bf16x4 ov;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = 128 * w + 32 * ct + 8 * q + 4 * h;
-          const f32x4 v{o[t][ct][4 * q], o[t][ct][4 * q + 1], o[t][ct][4 * q + 2], o[t][ct][4 * q + 3]};
-          if constexpr (FINAL) {
-            bf16x4 ov;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(v[i] * sc);
-            *(bf16x4*)(a.out + orow * kValue + col) = ov;
-          } else {
-            const int64_t prow = (int64_t)split * a.batch * R + orow;
-            *(f32x4*)(a.part_out + prow * kValue + col) = v * sc;
-          }
+          for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(v[i] * sc);
+          *(bf16x4*)(a.out + orow * kValue + col) = ov;
+        } else {
+          const int64_t prow = (int64_t)split * a.batch * R + orow;
+          *(f32x4*)(a.part_out + prow * kValue + col) = v * sc;
         }
-      if (w == 0 && h == 0) {
-        const float lv = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
-        if constexpr (FINAL) a.lse[orow] = lv;
-        else a.part_lse[(int64_t)split * a.batch * R + orow] = lv;
       }
+    if (v4 == 0 && h == 0) {
+      const float lv = (l_run > 0.f) ? ((grp ? mref1 : mref0) - kPShift + log2f(l_run)) * kLn2 : kNegInf;
+      if constexpr (FINAL) a.lse[orow] = lv;
+      else a.part_lse[(int64_t)split * a.batch * R + orow] = lv;
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -978,9 +1213,9 @@ hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) 
   if (FP8 && rows > 32 && rows <= 64) {
     dim3 grid(a.num_splits, a.batch);
     if (final_out)
-      hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kF8Threads), 0, stream, a);
     else
-      hipLaunchKernelGGL(split_kernel_f8x64<false>, grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(split_kernel_f8x64<false>, grid, dim3(kF8Threads), 0, stream, a);
     return hipGetLastError();
   }
   if (rows <= 16) return launch_layout<kLayout16, FP8>(a, final_out, stream);
