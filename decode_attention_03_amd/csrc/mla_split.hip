@@ -732,6 +732,22 @@ __device__ __forceinline__ void read_pv_f8(uint32_t vaddr, uint32_t paddr, u32x2
       : "v"(vaddr), "v"(paddr));
 }
 
+// Key operands of two consecutive k-steps (offsets OFF and OFF + 64).
+template <int OFF>
+__device__ __forceinline__ void read_k2_f8(uint32_t a0, uint32_t a1, i32x8& k0, i32x8& k1) {
+  u32x4 v0, v1, v2, v3;
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%6\n\t"
+      "ds_read_b128 %1, %5 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 64));
+  k0 = __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+  k1 = __builtin_bit_cast(i32x8, u32x8{v2[0], v2[1], v2[2], v2[3], v3[0], v3[1], v3[2], v3[3]});
+}
+
 template <int CT>
 __device__ __forceinline__ void read_v_f8(uint32_t vaddr, u32x2 (&r)[4]) {
   asm volatile(
@@ -860,24 +876,16 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int myrow = 32 * grp + r32;
   const int lim = L - a.num_q + myrow / H + 1;   // visible: position < lim
 
-  // ---- a2: copies.  Tile T goes to LDS buffer T % 3.  Waves 0..3 copy the
-  // tiles with T even and waves 4..7 those with T odd, wave w copying page w % 4
-  // (nine wave-wide one-KiB loads from one buffer descriptor), so each wave has
-  // at most one page in flight and two tiles are in flight per workgroup.  A
-  // page outside the split, or the positions past seq_len in the last page, lie
-  // outside the buffer range and are written to LDS as zeros by the copy itself.
-  const int cpar = w >> 2;
-  uint32_t voff[kWaveLoads];
-#pragma unroll
-  for (int c = 0; c < kWaveLoads; ++c) {
-    const uint32_t slot = 64 * c + lane;
-    const uint32_t row = slot / G::kChunksPerRow;
-    const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
-    voff[c] = row * G::kRowB + x * 16;
-  }
-  // Page-table entry of the page copied from tile T, loaded two tiles ahead
-  // with a vector load (entries past the sequence are clamped to its last page
-  // and not used).
+  // ---- a2: copies.  Tile T goes to LDS buffer T % 3; wave w copies page
+  // w % 4 (nine wave-wide one-KiB loads from one buffer descriptor).  Tiles 0
+  // and 1 are copied in the prologue (waves 0..3 tile 0, waves 4..7 tile 1);
+  // tile T >= 2 is copied by group 1 at E(T - 2), while it runs its softmax,
+  // so the copy issue never sits on the MFMA-role path and two tiles are in
+  // flight.  A page outside the split, or the positions past seq_len in the
+  // last page, lie outside the buffer range and are written to LDS as zeros by
+  // the copy itself.
+  // Page-table entry of page v4 of tile T (entries past the sequence are
+  // clamped to its last page and not used).
   const int32_t* pt_b = a.page_table + (int64_t)b * a.max_blocks;
   const int plast = max(P - 1, 0);
   auto pt_load = [&](int T) -> int {
@@ -890,25 +898,32 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB), 0, bytes, kBufferRsrcWord3);
     uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + v4 * G::kPageB;
+    // per-lane source offsets, recomputed here rather than held in registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int c = 0; c < kWaveLoads; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16, voff[c], 0, 0, 0);
+    for (int c = 0; c < kWaveLoads; ++c) {
+      const uint32_t slot = 64 * c + ln;
+      const uint32_t row = slot / G::kChunksPerRow;
+      const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16,
+                                               row * G::kRowB + x * 16, 0, 0, 0);
+    }
   };
-  // Vector-memory order of a wave: PT(T + 2), copies(T), then nothing until
-  // copies(T) are waited for (vmcnt(0)) at the start of E(T).
 
   // ---- query: q * 2^e = q1 + q2 (FP8), dims 64(ks0 + ks) + 32h + j of row `myrow`.
   // The query loads go out before the first copies (vmcnt counts in issue
   // order), so waiting for them leaves the copies in flight.
   i32x8 q1[5], q2[5];
   float q_unscale;
-  int ptc;   // page-table entries of the next tile to copy
+  int ptA, ptB;   // group 1: page-table entries of the next two tiles to copy
   {
     const bool real = myrow < R && ntiles > 0;   // empty splits skip the query work
     const uint16_t* qp = a.q + ((int64_t)b * R + (real ? myrow : 0)) * kLatent + 32 * h;
     const uint32_t keep = real ? 0xFFFFFFFFu : 0u;
-    const int pt0 = pt_load(cpar);
-    ptc = pt_load(cpar + 2);
+    const int pt0 = pt_load(grp);
+    ptA = pt_load(2);
+    ptB = pt_load(3);
     u32x4 qv[5][4];
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks) {
@@ -918,7 +933,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       for (int c = 0; c < 4; ++c) qv[ks][c] = *(const u32x4*)(qp + 64 * kk + 8 * c);
     }
     asm volatile("" ::: "memory");   // keep the query loads ahead of the copies
-    issue_tile(cpar, pt0);
+    issue_tile(grp, pt0);
     __builtin_amdgcn_sched_barrier(0);   // and the copies ahead of the query arithmetic
     float mx = 0.f;
 #pragma unroll
@@ -993,26 +1008,25 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     const uint32_t kb1 = (uint32_t)(uintptr_t)LDS_PTR(
         const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h + 1, 0) + 64 * ks0);
     // the reads of step ks + 1 run while the two MFMAs of step ks execute
-    i32x8 kc = read_k_f8<0>(kb0, kb1);
-    s = mfma_f8(kc, q1[0], s);
-    s = mfma_f8(kc, q2[0], s);
+    // k-steps in pairs: one LDS round trip per two steps; the reads of a pair
+    // run while the MFMAs of the previous pair drain
+    i32x8 ka, kb;
+    read_k2_f8<0>(kb0, kb1, ka, kb);
+    s = mfma_f8(ka, q1[0], s);
+    s = mfma_f8(ka, q2[0], s);
+    s = mfma_f8(kb, q1[1], s);
+    s = mfma_f8(kb, q2[1], s);
     __builtin_amdgcn_sched_barrier(0);
-    kc = read_k_f8<64>(kb0, kb1);
-    s = mfma_f8(kc, q1[1], s);
-    s = mfma_f8(kc, q2[1], s);
-    __builtin_amdgcn_sched_barrier(0);
-    kc = read_k_f8<128>(kb0, kb1);
-    s = mfma_f8(kc, q1[2], s);
-    s = mfma_f8(kc, q2[2], s);
-    __builtin_amdgcn_sched_barrier(0);
-    kc = read_k_f8<192>(kb0, kb1);
-    s = mfma_f8(kc, q1[3], s);
-    s = mfma_f8(kc, q2[3], s);
+    read_k2_f8<128>(kb0, kb1, ka, kb);
+    s = mfma_f8(ka, q1[2], s);
+    s = mfma_f8(ka, q2[2], s);
+    s = mfma_f8(kb, q1[3], s);
+    s = mfma_f8(kb, q2[3], s);
     __builtin_amdgcn_sched_barrier(0);
     if (!dh) {
-      kc = read_k_f8<256>(kb0, kb1);
-      s = mfma_f8(kc, q1[4], s);
-      s = mfma_f8(kc, q2[4], s);
+      ka = read_k_f8<256>(kb0, kb1);
+      s = mfma_f8(ka, q1[4], s);
+      s = mfma_f8(ka, q2[4], s);
     }
     // elements 8..15 belong to the partner wave; elements 0..7 stay for softmax
     xbuf[w][0][lane] = f32x4{s[8], s[9], s[10], s[11]};
@@ -1096,9 +1110,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // Start of the phase after group gx's softmax: move gx's reference maxima
   // where a tile maximum passed them by more than 2^kSlack, and in that (rare,
   // workgroup-uniform) case let gx recompute its probabilities.
-  auto check = [&](int gx) {
+  // Returns the group's row sums of that softmax when gx is this wave's group.
+  auto check = [&](int gx) -> float {
     const float nm = fmaxf(fmaxf(red_max[4 * gx][r32], red_max[4 * gx + 1][r32]),
                            fmaxf(red_max[4 * gx + 2][r32], red_max[4 * gx + 3][r32]));
+    auto sums = [&]() {
+      return (red_sum[4 * grp][r32] + red_sum[4 * grp + 1][r32]) +
+             (red_sum[4 * grp + 2][r32] + red_sum[4 * grp + 3][r32]);
+    };
+    float sm = grp == gx ? sums() : 0.f;   // read together with the maxima
     const float mo = gx ? mref1 : mref0;
     const bool ov = nm > mo + kSlack;
     if (__any(ov)) {
@@ -1116,13 +1136,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       lds_barrier();   // every wave has read the maxima (and the first sums)
       if (grp == gx) probs(mn);
       lds_barrier();
+      if (grp == gx) sm = sums();
     }
+    return sm;
   };
 
   // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127.
-  auto pv = [&]() {
-    l_run += (red_sum[4 * grp][r32] + red_sum[4 * grp + 1][r32]) +
-             (red_sum[4 * grp + 2][r32] + red_sum[4 * grp + 3][r32]);
+  auto pv = [&](float row_sum) {
+    l_run += row_sum;
     i32x8 pf[2];
     read_p32_f8((uint32_t)(uintptr_t)LDS_PTR(const uint8_t, pg_lds + r32 * kPRB + 32 * h), pf);
     // written out: a rolled loop here makes the compiler rotate the four
@@ -1142,22 +1163,33 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // T = (hs - g) / 2), odd -> softmax of tile T = (hs - g - 1) / 2.  At each
   // half-step the group that ran its softmax in the previous one (g = hs % 2)
   // is checked first.
+  // Tiles 0 and 1 (the prologue copies) have landed before the loop.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
-    const bool mine = (hs & 1) == 0 && ((hs >> 1) & 1) == cpar;   // this wave copied tile hs / 2
-    if (mine) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    const bool copier = grp == 1 && (hs & 1) == 0;
+    // Group 1's vector-memory order: ... PT(T + 2), copies(T), PT(T + 3),
+    // copies(T + 1) ...  Before E(T), T >= 2, copies(T) must have landed
+    // while PT(T + 3) and copies(T + 1) may still be in flight.
+    if (copier && hs >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads + 1));
     lds_barrier();
-    if (mine) {
+    if (copier) {
       const int it = hs >> 1;
-      const int ptn = pt_load(it + 4);
+      int cur;
+      if (it & 1) {
+        cur = ptB;
+        ptB = pt_load(it + 4);
+      } else {
+        cur = ptA;
+        ptA = pt_load(it + 4);
+      }
       asm volatile("" ::: "memory");   // keep PT(it + 4) ahead of the copies
-      issue_tile(it + 2, ptc);
-      ptc = ptn;
+      issue_tile(it + 2, cur);
     }
-    if (hs >= 2) check(hs & 1);
+    const float row_sum = hs >= 2 ? check(hs & 1) : 0.f;
     const int st = hs - grp;
     if (st >= 0 && (st & 1) == 0) {
       const int T = st >> 1;
-      if (T >= 1) pv();
+      if (T >= 1) pv(row_sum);
       if (T < ntiles) qk(T);
     } else if (st >= 1) {
       const int T = (st - 1) >> 1;
