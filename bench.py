@@ -378,12 +378,24 @@ def main():
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     _log(f"eager: {eager_ms:.3f} ms per step")
 
-    # Timed region: the step captured once as a HIP graph (the library neither
-    # allocates nor synchronises, so it is capturable) and replayed K times;
-    # this removes host launch overhead, as decode serving does.
+    # Timed region: the step captured as a HIP graph (the library neither
+    # allocates nor synchronises, so it is capturable) and replayed; this
+    # removes host launch overhead, as decode serving does.  A graph holds
+    # `reps` consecutive steps (at least 24 layer calls) so that the graph
+    # launch itself is amortised for small workloads; a timed step is still
+    # one pass over the batch.
+    reps = max(1, -(-24 // n_layers))
+
+    def repeat(fn):
+        def run():
+            for _ in range(reps):
+                fn()
+        return run
+
     stream = torch.cuda.Stream(device=dev)
     graphs = {}
-    for name, fn in (("step", step), ("split", split_only), ("merge", merge_only)):
+    for name, fn in (("step", repeat(step)), ("split", repeat(split_only)),
+                     ("merge", repeat(merge_only))):
         stream.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(stream):
             fn()  # warm the capture stream
@@ -396,12 +408,13 @@ def main():
     for _ in range(args.warmup):
         graphs["step"].replay()
     torch.cuda.synchronize()
+    n_replays = max(1, -(-args.steps // reps))
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(n_replays):
         graphs["step"].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = elapsed * 1e3 / (n_replays * reps)
     _log(f"graph replay: {ms_per_step:.3f} ms per step")
 
     alg = [workloads.algorithmic_bytes(l.seq_lens.cpu().numpy(), l.num_q, l.heads, l.kv_dtype)
@@ -416,19 +429,19 @@ def main():
     # graphs holding only the split kernels, or only the merge kernels.
     cur = torch.cuda.current_stream(dev)
 
-    def timed(g, reps):
+    def timed(g, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(args.warmup):
             g.replay()
         e0.record(cur)
-        for _ in range(reps):
+        for _ in range(n):
             g.replay()
         e1.record(cur)
         e1.synchronize()
-        return e0.elapsed_time(e1) / reps / n_layers * 1e3  # us per kernel launch
+        return e0.elapsed_time(e1) / (n * reps) / n_layers * 1e3  # us per kernel launch
 
-    split_us = timed(graphs["split"], args.steps)
-    merge_us = timed(graphs["merge"], args.steps) if S > 1 else 0.0
+    split_us = timed(graphs["split"], n_replays)
+    merge_us = timed(graphs["merge"], n_replays) if S > 1 else 0.0
     split_alg = float(np.mean(alg))     # one split launch processes one layer's batch
     achieved = split_alg / (split_us * 1e-6) / 1e9
     traffic = _traffic(config_tag(args.config), S)
@@ -472,8 +485,10 @@ def main():
             "mfma_tflops_algorithmic": round(sum(flops) / (ms_per_step * 1e-3) / 1e12, 2),
             "split_kernel_us": round(split_us, 3),
             "merge_kernel_us": round(merge_us, 3),
-            "timing": "HIP graph of the 24-layer step replayed K times; per-kernel times from "
-                      "graphs of one kernel kind, HIP events on the launch stream",
+            "timing": f"HIP graph of {reps} step(s) ({reps * n_layers} layer calls) replayed; "
+                      "per-kernel times from graphs of one kernel kind, HIP events on the "
+                      "launch stream",
+            "steps_timed": n_replays * reps,
             "eager_ms_per_step": round(eager_ms, 4),
         },
         "roofline": {

@@ -12,8 +12,17 @@ namespace {
 
 thread_local int32_t g_last_hip_error = 0;
 
-constexpr int kTargetWorkgroups = 512;  // two workgroups per CU on 256 CUs
-constexpr int kMinPagesPerSplit = 4;    // one 64-position tile
+// Automatic split count.  One split workgroup occupies a CU (its LDS).  A
+// batch of many sequences of unequal length balances better over several
+// rounds of workgroups (up to four rounds over the 256 CUs of an MI355X from
+// 64 sequences on); a few sequences get one full round, since every extra
+// split adds partials to write and merge.  A split keeps at least eight
+// 64-position tiles to amortise its fixed cost (query preparation, first
+// tile, epilogue).
+constexpr int kComputeUnits = 256;
+constexpr int kMaxRounds = 4;
+constexpr int kSeqsPerRound = 16;
+constexpr int kMinPagesPerSplit = 32;
 
 mla_status check_params(const mla_params* p, int max_q) {
   if (!p) return MLA_ERR_NULL_ARG;
@@ -33,10 +42,17 @@ int32_t choose_splits(const mla_params* p) {
   int64_t max_len = p->max_seq_len_hint > 0 ? p->max_seq_len_hint
                                             : (int64_t)p->max_blocks_per_seq * mla::kPage;
   int64_t pages = (max_len + mla::kPage - 1) / mla::kPage;
-  int64_t s = (kTargetWorkgroups + p->batch - 1) / p->batch;
+  int64_t rounds = p->batch / kSeqsPerRound;
+  if (rounds < 1) rounds = 1;
+  if (rounds > kMaxRounds) rounds = kMaxRounds;
+  int64_t s = (rounds * kComputeUnits + p->batch - 1) / p->batch;
   int64_t cap = pages / kMinPagesPerSplit;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
+  // between one and two rounds of workgroups: use exactly one full round
+  // rather than leave most CUs idle during a short second one
+  const int64_t wg = s * p->batch;
+  if (wg > kComputeUnits && wg < 2 * kComputeUnits) s = kComputeUnits / p->batch;
   if (s > mla::kMaxSplits) s = mla::kMaxSplits;
   if (s < 1) s = 1;
   return (int32_t)s;

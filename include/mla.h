@@ -105,7 +105,10 @@ typedef struct {
 } mla_params;
 
 /* Split count the library uses for these parameters (>= 1), or 0 if the
- * parameters are invalid.  Depends only on host-side values. */
+ * parameters are invalid.  Depends only on host-side values: with num_splits
+ * = 0 it is min(ceil(256 * R / B), pages / 32), at least 1, for
+ * R = clamp(B / 16, 1, 4) rounds of 256 workgroups and pages = ceil(hint / 16);
+ * when B * S falls between one and two rounds, S = 256 / B (one full round). */
 int32_t mla_num_splits(const mla_params* p);
 
 /* Bytes of workspace mla_decode / mla_verify need: the partials of all splits

@@ -59,12 +59,18 @@ def test_status_strings(lib):
 
 
 def test_split_planning(lib):
-    # long-context layer: 4 sequences -> 128 splits (512 workgroups), capped by pages / 4
-    assert lib.mla_num_splits(ctypes.byref(params())) == 128
+    # long-context layer: 4 sequences (one round of 256 workgroups) x 2219 pages
+    # -> min(64, 69) = 64 splits
+    assert lib.mla_num_splits(ctypes.byref(params())) == 64
+    # 4 x 142,000 positions (8875 pages) -> still one round: 64
+    assert lib.mla_num_splits(ctypes.byref(params(max_seq_len_hint=142000))) == 64
     assert lib.mla_num_splits(ctypes.byref(params(num_splits=8))) == 8
-    assert lib.mla_num_splits(ctypes.byref(params(batch=64, max_seq_len_hint=65536))) == 8
+    # 64 sequences up to 4096 pages -> min(16, 128) = 16 (1024 workgroups)
+    assert lib.mla_num_splits(ctypes.byref(params(batch=64, max_seq_len_hint=65536))) == 16
+    # 32 sequences (two rounds) up to 512 pages -> min(16, 16) = 16
+    assert lib.mla_num_splits(ctypes.byref(params(batch=32, max_seq_len_hint=8192))) == 16
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=256,
-                                                  max_blocks_per_seq=16))) == 4
+                                                  max_blocks_per_seq=16))) == 1
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=20))) == 1
     assert lib.mla_num_splits(ctypes.byref(params(num_heads=17))) == 0
     S = 8
