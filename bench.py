@@ -42,7 +42,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c5b"])
+    ap.add_argument("--config", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c5b", "c6"])
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -252,7 +252,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
 
 TAGS = {"long_ctx_fp8_4x35500_q3_h12": "c5", "long_ctx_fp8_4x142000_q3_h12": "c5b",
         "fp8_verify_b64_q3_h12": "c4", "bf16_verify_b32_q3_h12": "c3",
-        "bf16_decode_b32_q1_h12": "c2", "tiny_decode_b1_l256": "c1"}
+        "bf16_decode_b32_q1_h12": "c2", "tiny_decode_b1_l256": "c1",
+        "dcp8_fp8_verify_b64_q3_h96": "c6"}
 
 
 def tag_config(tag):
@@ -448,8 +449,10 @@ def main():
     # executed MFMA work of the split kernel (padded rows, two-term fp8 operands)
     fp8 = first.kv_dtype == "fp8"
     rows = first.num_q * first.heads
-    exec_rows = 64 if (fp8 and 32 < rows <= 64) else 16 if rows <= 16 else 48 if rows <= 48 else rows
-    terms = 2 if (fp8 and 32 < rows <= 64) else 1
+    # row blocks: 64 for the fp8 kernel (above 32 rows), else 16 or 48
+    rblock = 64 if (fp8 and rows > 32) else 16 if rows <= 16 else 48
+    exec_rows = rblock * -(-rows // rblock)
+    terms = 2 if (fp8 and rows > 32) else 1
     positions = sum(int(l.seq_lens.sum().item()) for l in layers) / n_layers
     mfma_exec = positions * exec_rows * terms * 2 * (576 + 512)
     mfma_peak = 5000.0 if terms == 2 else 2500.0

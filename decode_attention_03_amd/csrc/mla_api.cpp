@@ -45,14 +45,19 @@ int32_t choose_splits(const mla_params* p) {
   int64_t rounds = p->batch / kSeqsPerRound;
   if (rounds < 1) rounds = 1;
   if (rounds > kMaxRounds) rounds = kMaxRounds;
-  int64_t s = (rounds * kComputeUnits + p->batch - 1) / p->batch;
+  // query rows are processed in blocks (64 rows for FP8 verify, else 48 or
+  // 16), each a workgroup of its own over the same split
+  const int64_t rows = (int64_t)p->num_q_tokens * p->num_heads;
+  const int64_t rblock = (p->kv_dtype == MLA_KV_FP8_E4M3 && rows > 32) ? 64 : (rows <= 16 ? 16 : 48);
+  const int64_t units = (int64_t)p->batch * ((rows + rblock - 1) / rblock);
+  int64_t s = (rounds * kComputeUnits + units - 1) / units;
   int64_t cap = pages / kMinPagesPerSplit;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
   // between one and two rounds of workgroups: use exactly one full round
   // rather than leave most CUs idle during a short second one
-  const int64_t wg = s * p->batch;
-  if (wg > kComputeUnits && wg < 2 * kComputeUnits) s = kComputeUnits / p->batch;
+  const int64_t wg = s * units;
+  if (wg > kComputeUnits && wg < 2 * kComputeUnits) s = kComputeUnits / units;
   if (s > mla::kMaxSplits) s = mla::kMaxSplits;
   if (s < 1) s = 1;
   return (int32_t)s;

@@ -22,8 +22,8 @@ constexpr int kTilePages = kWaves;
 constexpr int kTilePos = kTilePages * kPage;
 
 // Largest query-token count per launch and largest head count per token.
-constexpr int kMaxQ = 3;
-constexpr int kMaxHeads = 16;
+constexpr int kMaxQ = 8;
+constexpr int kMaxHeads = 128;
 constexpr int kMaxSplits = 256;
 
 struct SplitArgs {

@@ -261,8 +261,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // tile row (layout 16); B = the 16-row tile row 32 + r16 (layout 48).
   const int rowA = L16 ? r16 : r32;
   const int rowB = 32 + r16;
-  const int limA = L - a.num_q + rowA / H + 1;   // visible: position < lim
-  const int limB = L - a.num_q + rowB / H + 1;
+  // rows rb0 .. rb0 + RPAD - 1 of the Q*H query rows are this workgroup's
+  const int rb0 = (int)blockIdx.z * RPAD;
+  const int limA = L - a.num_q + (rb0 + rowA) / H + 1;   // visible: position < lim
+  const int limB = L - a.num_q + (rb0 + rowB) / H + 1;
 
   // ---- query fragments (B operand of S^T = K Q^T), kept in registers.
   //      layout 16:             row r16,      dims 32ks + 8g,          ks < 18
@@ -271,8 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   u32x4 qreg[kQRegs];
   {
     const int qrow = L16 ? r16 : (t32 ? r32 : rowB);
-    const bool real = qrow < R;
-    const uint16_t* qp = a.q + ((int64_t)b * R + (real ? qrow : 0)) * kLatent;
+    const bool real = rb0 + qrow < R;
+    const uint16_t* qp = a.q + ((int64_t)b * R + (real ? rb0 + qrow : 0)) * kLatent;
 #pragma unroll
     for (int ks = 0; ks < kQRegs; ++ks) {
       int d0;
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   }
 
   // ---- a7: epilogue (real rows only).
-  const int64_t row_base = (int64_t)b * R;
+  const int64_t row_base = (int64_t)b * R + rb0;
   auto store4 = [&](int r, int col, f32x4 v, float sc) {
     const int64_t orow = row_base + r;
     if constexpr (FINAL) {
@@ -597,13 +599,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const float scA = l_runA > 0.f ? a.out_scale / l_runA : 0.f;
   const int col0 = 128 * w;
   if constexpr (L16) {
-    if (r16 < R) {
+    if (rb0 + r16 < R) {
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) store4(r16, col0 + 16 * ct + 4 * g, o16a[ct], scA);
       if (w == 0 && g == 0) store_lse(r16, m_runA, l_runA);
     }
   } else {
-    if (r32 < R) {
+    if (rb0 + r32 < R) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -613,7 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         }
       if (w == 0 && h == 0) store_lse(r32, m_runA, l_runA);
     }
-    if (rowB < R) {
+    if (rb0 + rowB < R) {
       const float scB = l_runB > 0.f ? a.out_scale / l_runB : 0.f;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) store4(rowB, col0 + 16 * ct + 4 * g, o16b[ct], scB);
@@ -873,7 +875,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
   const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
 
-  const int myrow = 32 * grp + r32;
+  // rows 64 * blockIdx.z .. + 63 of the Q*H query rows are this workgroup's
+  const int myrow = 64 * (int)blockIdx.z + 32 * grp + r32;
   const int lim = L - a.num_q + myrow / H + 1;   // visible: position < lim
 
   // ---- a2: copies.  Tile T goes to LDS buffer T % 3; wave w copies page
@@ -1231,7 +1234,9 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 
 template <int LAYOUT, bool FP8>
 hipError_t launch_layout(const SplitArgs& a, bool final_out, hipStream_t stream) {
-  dim3 grid(a.num_splits, a.batch);
+  const int rows = a.num_q * a.heads;
+  const int rpad = LAYOUT == kLayout16 ? 16 : 48;
+  dim3 grid(a.num_splits, a.batch, (rows + rpad - 1) / rpad);
   if (final_out)
     hipLaunchKernelGGL((split_kernel<LAYOUT, FP8, true>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -1242,8 +1247,8 @@ hipError_t launch_layout(const SplitArgs& a, bool final_out, hipStream_t stream)
 template <bool FP8>
 hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) {
   const int rows = a.num_q * a.heads;
-  if (FP8 && rows > 32 && rows <= 64) {
-    dim3 grid(a.num_splits, a.batch);
+  if (FP8 && rows > 32) {
+    dim3 grid(a.num_splits, a.batch, (rows + 63) / 64);
     if (final_out)
       hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kF8Threads), 0, stream, a);
     else
@@ -1251,8 +1256,7 @@ hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) 
     return hipGetLastError();
   }
   if (rows <= 16) return launch_layout<kLayout16, FP8>(a, final_out, stream);
-  if (rows <= 48) return launch_layout<kLayout48, FP8>(a, final_out, stream);
-  return hipErrorInvalidValue;
+  return launch_layout<kLayout48, FP8>(a, final_out, stream);
 }
 
 }  // namespace

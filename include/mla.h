@@ -33,9 +33,10 @@
  * no visible position has lse = -inf and output 0.
  *
  * Head padding ("Inside Kimi K3 optimization", section "4. MLA"; "Kimi K3 on
- * AMD MI355X", section "What had to be fixed"): heads are padded to 16 rows
- * per query token inside the kernel with zero queries; pad rows are never
- * read from or written to caller memory.
+ * AMD MI355X", section "What had to be fixed"): the Q*H query rows (token-major,
+ * r = j*H + h) are processed in blocks of 16, 48 or 64 rows, the last block
+ * padded inside the kernel with zero queries; pad rows are never read from or
+ * written to caller memory.
  *
  * Layouts (all row-major, contiguous, caller-owned device memory)
  * --------------------------------------------------------------
@@ -94,8 +95,8 @@ typedef enum {
 
 typedef struct {
   int32_t batch;              /* B >= 1 */
-  int32_t num_q_tokens;       /* Q: 1 for mla_decode; 1..3 for mla_verify */
-  int32_t num_heads;          /* H: 1..16 (12 per TP8 rank); padded to 16 rows per token */
+  int32_t num_q_tokens;       /* Q: 1 for mla_decode; 1..8 for mla_verify */
+  int32_t num_heads;          /* H: 1..128 (12 per TP8 rank, 96 for DCP8-shaped attention) */
   int32_t num_blocks;         /* pool blocks in kv_cache, >= 1 */
   int32_t max_blocks_per_seq; /* page_table row stride, >= 1 */
   int32_t max_seq_len_hint;   /* largest seq_len the caller expects; 0 = 16 * max_blocks_per_seq.
@@ -106,9 +107,11 @@ typedef struct {
 
 /* Split count the library uses for these parameters (>= 1), or 0 if the
  * parameters are invalid.  Depends only on host-side values: with num_splits
- * = 0 it is min(ceil(256 * R / B), pages / 32), at least 1, for
- * R = clamp(B / 16, 1, 4) rounds of 256 workgroups and pages = ceil(hint / 16);
- * when B * S falls between one and two rounds, S = 256 / B (one full round). */
+ * = 0 it is min(ceil(256 * R / U), pages / 32), at least 1, for
+ * R = clamp(B / 16, 1, 4) rounds of 256 workgroups, U = B times the number of
+ * query-row blocks (blocks of 64 rows for FP8 with more than 32 rows Q*H, else
+ * 48, or 16 for at most 16 rows) and pages = ceil(hint / 16); when U * S falls
+ * between one and two rounds, S = 256 / U (one full round). */
 int32_t mla_num_splits(const mla_params* p);
 
 /* Bytes of workspace mla_decode / mla_verify need: the partials of all splits

@@ -72,7 +72,10 @@ def test_split_planning(lib):
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=256,
                                                   max_blocks_per_seq=16))) == 1
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=20))) == 1
-    assert lib.mla_num_splits(ctypes.byref(params(num_heads=17))) == 0
+    assert lib.mla_num_splits(ctypes.byref(params(num_heads=129))) == 0
+    # 96 heads x 3 tokens = 288 FP8 rows -> 5 row blocks of 64: 4 x 5 = 20 units
+    # -> min(ceil(256 / 20) = 13, 69) = 13 -> 260 workgroups -> one round: 12
+    assert lib.mla_num_splits(ctypes.byref(params(num_heads=96))) == 12
     S = 8
     rows = 4 * 3 * 12
     expect = ((S * rows * 512 * 4 + 255) // 256) * 256 + ((S * rows * 4 + 255) // 256) * 256
@@ -98,13 +101,13 @@ def test_validation_errors(lib, entry):
     assert _verify(lib, None, entry=entry) == NULL
     for i in range(6):
         assert _verify(lib, params(num_q_tokens=q1), entry=entry, nulls=(i,)) == NULL
-    for bad in (dict(batch=0), dict(num_q_tokens=0), dict(num_q_tokens=4), dict(num_heads=0),
+    for bad in (dict(batch=0), dict(num_q_tokens=0), dict(num_q_tokens=9), dict(num_heads=0),
                 dict(num_blocks=0), dict(max_blocks_per_seq=0), dict(max_seq_len_hint=-1),
                 dict(num_splits=-1), dict(num_splits=257)):
         d = dict(num_q_tokens=q1)
         d.update(bad)
         assert _verify(lib, params(**d), entry=entry) == SHAPE, bad
-    assert _verify(lib, params(num_q_tokens=q1, num_heads=17), entry=entry) == UNSUP
+    assert _verify(lib, params(num_q_tokens=q1, num_heads=129), entry=entry) == UNSUP
     assert _verify(lib, params(num_q_tokens=q1, kv_dtype=2), entry=entry) == DTYPE
     assert _verify(lib, params(num_q_tokens=q1), ss=float("nan"), entry=entry) == SCALE
     assert _verify(lib, params(num_q_tokens=q1), ss=float("inf"), entry=entry) == SCALE

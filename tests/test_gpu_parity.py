@@ -50,6 +50,47 @@ def test_small_cases(gpu_lib, case):
     compare(out, lse, ro, rl, str(case))
 
 
+# Query rows beyond one block: row blocks of 64 (FP8, more than 32 rows), 48
+# or 16 (generic kernel), including a partial last block and single-split
+# (direct bf16 output) launches over several row blocks.
+WIDE_CASES = [
+    # (seq_lens, Q, H, kv_dtype, num_splits)
+    ([300, 1500], 3, 96, "fp8", 0),
+    ([300, 1500], 3, 96, "bf16", 0),
+    ([65, 700], 8, 12, "fp8", 3),
+    ([65, 700], 8, 12, "bf16", 3),
+    ([129, 40], 5, 16, "fp8", 2),
+    ([257], 1, 128, "bf16", 1),
+    ([257], 1, 128, "fp8", 2),
+    ([100], 1, 20, "fp8", 0),
+    ([8, 9], 8, 3, "bf16", 0),
+    ([33], 7, 16, "fp8", 1),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[f"{c[3]}-Q{c[1]}-H{c[2]}-S{c[4]}-{len(c[0])}seq"
+                                                   for c in WIDE_CASES])
+def test_wide_row_blocks(gpu_lib, case):
+    lens, nq, nh, dt, S = case
+    _say(f"wide case {case}")
+    inp = make_inputs(lens, nq, nh, dt, seed=7 * sum(lens) + nq + nh, device="cuda",
+                      spare_blocks=2, poison=True)
+    out, lse = run_verify(gpu_lib, inp, num_splits=S)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, str(case))
+
+
+def test_c6_dcp8_shaped_sampled(gpu_lib):
+    _say("config c6")
+    inp = make_config("c6", device="cuda")
+    out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=8192)
+    lens = inp.seq_lens.cpu().numpy()
+    idx = sorted(set(np.random.default_rng(606).choice(inp.batch, size=4, replace=False).tolist())
+                 | {int(np.argmax(lens)), int(np.argmin(lens))})
+    ro, rl, _ = oracle_out(inp, idx)
+    compare(out[idx], lse[idx], ro, rl, f"c6 seqs {idx}")
+
+
 def test_decode_entry_point(gpu_lib):
     inp = make_inputs([50, 900, 2049], 1, 12, "fp8", seed=5, device="cuda")
     out, lse = gpu_lib.decode(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,

@@ -56,6 +56,11 @@ CONFIGS = {
     "c5b": dict(seed=5, batch=4, num_q=3, heads=12, kv_dtype="fp8", seq_lo=142000, seq_hi=142000,
                 layers=24, chunks=8,
                 desc="long-context, alternative reading: 24 layers x 4 x 142,000 fp8 positions"),
+    # one GPU's share under DCP8: all 96 heads (query all-gathered) over an eighth
+    # of the c4 positions of each sequence
+    "c6": dict(seed=6, batch=64, num_q=3, heads=96, kv_dtype="fp8", seq_lo=1024, seq_hi=8192,
+               desc="DCP8-shaped FP8 verify: B=64, Q=3 causal, H=96, L~U[1024,8192] "
+                    "(an eighth of the B=64 FP8 workload's history), fp8 e4m3 + scale"),
 }
 
 
