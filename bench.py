@@ -312,6 +312,50 @@ def _cpu_baseline(layers, budget_s):
                       f"host cores visible={cores}"}
 
 
+def _rank_merge(mla, first, dev, warmup, steps):
+    """The merge a rank runs under context parallelism over ranks = heads / 12
+    GPUs: after the exchange of partials it combines, for its own 12 heads,
+    one partial per rank.  Timed on seeded partials of that shape."""
+    import torch
+    ranks = first.heads // 12
+    rows = first.batch * first.num_q * 12
+    g = torch.Generator(device="cpu").manual_seed(606)
+    po = (torch.randn((ranks, rows * 512), generator=g) * 0.05).to(dev)
+    pl = (torch.randn((ranks, rows), generator=g) + 8.0).to(dev)
+    out = torch.empty((first.batch, first.num_q, 12, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((first.batch, first.num_q, 12), dtype=torch.float32, device=dev)
+
+    def run():
+        mla.merge(po.view(ranks, first.batch, first.num_q, 12, 512),
+                  pl.view(ranks, first.batch, first.num_q, 12), out=out, lse=lse)
+
+    per_graph = 20
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        run()
+    torch.cuda.current_stream(dev).wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(per_graph):
+            run()
+    for _ in range(warmup):
+        graph.replay()
+    cur = torch.cuda.current_stream(dev)
+    n = max(1, steps // per_graph)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(n):
+        graph.replay()
+    e1.record(cur)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) / (n * per_graph) * 1e3
+    nbytes = ranks * rows * (512 * 4 + 4) + rows * (512 * 2 + 4)
+    return {"partials": ranks, "rows": rows, "us": round(us, 3),
+            "gb_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "note": f"seeded partials; HIP graph of {per_graph} merges replayed, HIP events"}
+
+
 def main():
     args = _args()
     if args.summarize_profiles:
@@ -456,6 +500,22 @@ def main():
     positions = sum(int(l.seq_lens.sum().item()) for l in layers) / n_layers
     mfma_exec = positions * exec_rows * terms * 2 * (576 + 512)
     mfma_peak = 5000.0 if terms == 2 else 2500.0
+    # The split kernel is bound by HBM below the MFMA ridge (peak flops / 8 TB/s)
+    # and by the matrix cores above it (many heads, e.g. 96 heads at Q = 3).
+    intensity = sum(flops) / bytes_per_step
+    mfma_bound = intensity > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    split_flops = float(np.mean(flops))
+    if mfma_bound:
+        a_tf = split_flops / (split_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "split_kernel", "achieved": round(a_tf, 2),
+                    "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(a_tf / mfma_peak, 4),
+                    "traffic": None if traffic is None else round(traffic),
+                    "intensity_flop_per_byte": round(intensity, 1)}
+    else:
+        roofline = {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 2),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None if traffic is None else round(traffic),
+                    "intensity_flop_per_byte": round(intensity, 1)}
 
     line = {
         "metric": METRIC,
@@ -494,15 +554,7 @@ def main():
             "steps_timed": n_replays * reps,
             "eager_ms_per_step": round(eager_ms, 4),
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "split_kernel",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if traffic is None else round(traffic),
-        },
+        "roofline": roofline,
         "mfma_roofline": {
             "kernel": "split_kernel",
             "executed_tflops": round(mfma_exec / (split_us * 1e-6) / 1e12, 2),
@@ -514,6 +566,8 @@ def main():
         },
     }
     _log(f"split {split_us:.2f} us, merge {merge_us:.2f} us per launch")
+    if first.heads > 12 and first.heads % 12 == 0:
+        line["config"]["rank_merge"] = _rank_merge(mla, first, dev, args.warmup, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(layers, args.cpu_seconds)
     if args.copy_calibration:

@@ -187,7 +187,7 @@ mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_s
                      void* out, float* lse, void* stream) {
   if (!part_out || !part_lse || !out || !lse) return MLA_ERR_NULL_ARG;
   if (num_splits < 1 || num_splits > 4096) return MLA_ERR_BAD_SHAPE;
-  if (rows < 1 || rows > ((int64_t)1 << 30)) return MLA_ERR_BAD_SHAPE;
+  if (rows < 1 || rows > ((int64_t)1 << 28)) return MLA_ERR_BAD_SHAPE;   // grid: 4 workgroups per row
   mla::MergeArgs m{};
   m.part_out = part_out;
   m.part_lse = part_lse;

@@ -5,11 +5,15 @@
 // sections "1. Cache -- DCP" and "4. MLA"):
 //   lse = ln sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * o_s  -> bf16 (RNE).
 //
-// HBM-bound streaming.  One 256-thread workgroup per (row, 256-column half):
-//   1. the weights exp(lse_s - max) of all S partials are computed once into
-//      LDS (block-wide max and sum reductions);
-//   2. 64 column chunks (4 floats) x 4 split lanes stream the partial rows
-//      with independent 16-byte loads, and the 4 lanes are summed in LDS.
+// HBM-bound streaming of S partial rows per output row.  A 256-thread
+// workgroup holds one or more row slices; in each, LANES split lanes x
+// COLS/4 column chunks (4 floats) stream the partials with up to eight
+// independent 16-byte loads in flight per thread:
+//   S <= 8:  1 lane,  whole rows, two rows per workgroup
+//   S <= 32: 2 lanes, whole rows, one row per workgroup
+//   S > 32:  8 lanes, 128-column quarters, four workgroups per row
+// Per row slice, the weights exp(lse_s - max) are computed once into LDS
+// (S floats of dynamic LDS per slice), and the lanes are summed in LDS.
 #include <math.h>
 
 #include "mla_common.hpp"
@@ -22,85 +26,120 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kMergeThreads = 256;
-constexpr int kSplitLanes = kMergeThreads / 64;   // 4
-constexpr int kMaxCoef = 4096;                     // largest split count (the API bound)
+constexpr int kInFlight = 8;   // loads per thread per round
 
-__device__ __forceinline__ float block_max(float v, float* red) {
+// max / sum over the WPR waves of one row slice (waves w0 .. w0 + WPR - 1)
+template <int WPR, bool MAX>
+__device__ __forceinline__ float slice_reduce(float v, float* red) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float o = __shfl_xor(v, m);
+    v = MAX ? fmaxf(v, o) : v + o;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int w0 = w / WPR * WPR;
+  v = red[w0];
+#pragma unroll
+  for (int i = 1; i < WPR; ++i) v = MAX ? fmaxf(v, red[w0 + i]) : v + red[w0 + i];
   __syncthreads();
   return v;
 }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return v;
-}
-
+template <int LANES, int COLS>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
-  __shared__ float coef[kMaxCoef];
-  __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) f32x4 part[kSplitLanes][64];
+  constexpr int kChunks = COLS / 4;
+  constexpr int kTPR = LANES * kChunks;        // threads per row slice
+  constexpr int kRPW = kMergeThreads / kTPR;   // row slices per workgroup
+  constexpr int kSlices = kValue / COLS;       // workgroups per row
+  constexpr int kWPR = kTPR / 64;              // waves per row slice
+  static_assert(kTPR % 64 == 0 && kRPW * kTPR == kMergeThreads, "merge shape");
+  extern __shared__ float coef[];              // [kRPW][S]
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ __attribute__((aligned(16))) f32x4 part[kMergeThreads];
 
-  const int64_t row = (int64_t)blockIdx.x >> 1;
-  const int half = blockIdx.x & 1;
   const int tid = threadIdx.x;
+  const int rs = tid / kTPR;
+  const int t = tid % kTPR;
   const int S = a.num_splits;
+  const int64_t row = ((int64_t)blockIdx.x / kSlices) * kRPW + rs;
+  const int slice = (int)(blockIdx.x % kSlices);
+  const bool live = row < a.rows;
+  float* cf = coef + rs * S;
 
   float m = kNegInf;
-  for (int s = tid; s < S; s += kMergeThreads) m = fmaxf(m, a.part_lse[(int64_t)s * a.rows + row]);
-  m = block_max(m, red);
+  if (live)
+    for (int s = t; s < S; s += kTPR) m = fmaxf(m, a.part_lse[(int64_t)s * a.rows + row]);
+  m = slice_reduce<kWPR, true>(m, red);
 
   float wsum = 0.f;
-  for (int s = tid; s < S; s += kMergeThreads) {
-    const float ls = a.part_lse[(int64_t)s * a.rows + row];
-    const float wgt = (ls == kNegInf) ? 0.f : expf(ls - m);
-    coef[s] = wgt;
-    wsum += wgt;
-  }
-  wsum = block_sum(wsum, red);   // its barriers also publish coef[]
+  if (live)
+    for (int s = t; s < S; s += kTPR) {
+      const float ls = a.part_lse[(int64_t)s * a.rows + row];
+      const float wgt = (ls == kNegInf) ? 0.f : expf(ls - m);
+      cf[s] = wgt;
+      wsum += wgt;
+    }
+  wsum = slice_reduce<kWPR, false>(wsum, red);   // its barriers also publish coef[]
 
-  const int chunk = tid & 63;         // 4-float column chunk inside this half
-  const int lane_s = tid >> 6;        // split lane
-  const int col = half * 256 + 4 * chunk;
+  const int chunk = t % kChunks;
+  const int lane_s = t / kChunks;
+  const int col = slice * COLS + 4 * chunk;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  if (m != kNegInf) {
+  if (live && m != kNegInf) {
     const float* po = a.part_out + row * kValue + col;
-#pragma unroll 4
-    for (int s = lane_s; s < S; s += kSplitLanes) {
-      const float wgt = coef[s];
-      if (wgt != 0.f) {   // uniform branch: an empty partial is never read
-        const f32x4 v = *(const f32x4*)(po + (int64_t)s * a.rows * kValue);
-        acc += wgt * v;
+    const int64_t stride = a.rows * kValue;
+    for (int s0 = lane_s; s0 < S; s0 += LANES * kInFlight) {
+      f32x4 v[kInFlight];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        const int s = s0 + LANES * u;
+        v[u] = s < S ? *(const f32x4*)(po + s * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        const int s = s0 + LANES * u;
+        const float wgt = s < S ? cf[s] : 0.f;
+        // a partial of weight zero (empty split) contributes nothing, whatever it holds
+        if (wgt != 0.f) acc += wgt * v[u];
       }
     }
   }
-  part[lane_s][chunk] = acc;
-  __syncthreads();
-  if (lane_s == 0) {
-    const f32x4 t = (part[0][chunk] + part[1][chunk]) + (part[2][chunk] + part[3][chunk]);
+  if constexpr (LANES > 1) {
+    part[tid] = acc;
+    __syncthreads();
+    if (lane_s == 0) {
+#pragma unroll
+      for (int l = 1; l < LANES; ++l) acc += part[tid + l * kChunks];
+    }
+  }
+  if (live && lane_s == 0) {
     const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
     bf16x4 ov;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(t[i] * inv);
+    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc[i] * inv);
     *(bf16x4*)(a.out + row * kValue + col) = ov;
-    if (tid == 0 && half == 0) a.lse[row] = (wsum > 0.f) ? m + logf(wsum) : kNegInf;
+    if (t == 0 && slice == 0) a.lse[row] = (wsum > 0.f) ? m + logf(wsum) : kNegInf;
   }
+}
+
+template <int LANES, int COLS>
+hipError_t launch_shape(const MergeArgs& a, hipStream_t stream) {
+  constexpr int kRPW = kMergeThreads / (LANES * COLS / 4);
+  const int64_t groups = (a.rows + kRPW - 1) / kRPW;
+  const size_t lds = (size_t)kRPW * a.num_splits * sizeof(float);
+  hipLaunchKernelGGL((merge_kernel<LANES, COLS>), dim3((unsigned)(groups * (kValue / COLS))),
+                     dim3(kMergeThreads), lds, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(a.rows * 2)), dim3(kMergeThreads), 0, stream, a);
-  return hipGetLastError();
+  if (a.num_splits <= 8) return launch_shape<1, 512>(a, stream);
+  if (a.num_splits <= 32) return launch_shape<2, 512>(a, stream);
+  return launch_shape<8, 128>(a, stream);
 }
 
 }  // namespace mla

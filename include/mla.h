@@ -147,7 +147,9 @@ mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
  *     out[r][c] = bf16_rne( sum_s exp(part_lse[s][r] - lse[r]) * part_out[s][r][c] )
  * part_out fp32 [num_splits][rows][512], part_lse fp32 [num_splits][rows],
  * out bf16 [rows][512], lse fp32 [rows].  All partials -inf: out 0, lse -inf.
- * 1 <= num_splits <= 4096, rows >= 1. */
+ * 1 <= num_splits <= 4096, 1 <= rows <= 2^28; otherwise MLA_ERR_BAD_SHAPE.  A
+ * partial of weight zero (part_lse = -inf) is never used, whatever part_out
+ * holds for it. */
 mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_splits,
                      int64_t rows, void* out, float* lse, void* stream);
 

@@ -140,3 +140,4 @@ def test_split_and_merge_validation(lib):
     assert lib.mla_merge(FAKE, FAKE, 0, 10, FAKE, FAKE, None) == SHAPE
     assert lib.mla_merge(FAKE, FAKE, 4097, 10, FAKE, FAKE, None) == SHAPE
     assert lib.mla_merge(FAKE, FAKE, 4, 0, FAKE, FAKE, None) == SHAPE
+    assert lib.mla_merge(FAKE, FAKE, 4, (1 << 28) + 1, FAKE, FAKE, None) == SHAPE

@@ -170,15 +170,19 @@ def test_split_partials_match_oracle(gpu_lib):
             assert np.abs(got_o - ro[s, b]).max() <= 1e-2 * np.abs(ro[s, b]).max() + 1e-30
 
 
-def test_merge_matches_oracle(gpu_lib):
-    rng = np.random.default_rng(3)
-    S, rows = 13, 300
+@pytest.mark.parametrize("S", [1, 8, 13, 64, 129])
+def test_merge_matches_oracle(gpu_lib, S):
+    rng = np.random.default_rng(3 + S)
+    rows = 300
     po = rng.normal(size=(S, rows, 512)).astype(np.float32)
     pl = (rng.normal(size=(S, rows)) * 3).astype(np.float32)
     pl[rng.random(size=(S, rows)) < 0.2] = -np.inf
     pl[:, 7] = -np.inf          # a row with every partial empty
     po[np.isneginf(pl)] = 0.0
-    out, lse = gpu_lib.merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    # partials of weight zero must not be read into the result: poison them
+    po_dev = po.copy()
+    po_dev[np.isneginf(pl)] = np.nan
+    out, lse = gpu_lib.merge(torch.from_numpy(po_dev).cuda(), torch.from_numpy(pl).cuda())
     torch.cuda.synchronize()
     ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64))
     fin = np.isfinite(rl)
