@@ -12,6 +12,8 @@ from ._lib import (
     MLA_KV_FP8_E4M3,
     Params,
     decode,
+    kv_append,
+    kv_dynamic_scale,
     load,
     make_params,
     merge,
@@ -23,6 +25,7 @@ from ._lib import (
 from .build import LIB_PATH
 
 __all__ = [
-    "EXPORTS", "MLAError", "MLA_KV_BF16", "MLA_KV_FP8_E4M3", "Params", "decode", "load",
+    "EXPORTS", "MLAError", "MLA_KV_BF16", "MLA_KV_FP8_E4M3", "Params", "decode", "kv_append",
+    "kv_dynamic_scale", "load",
     "make_params", "merge", "num_splits", "split", "verify", "workspace_size", "LIB_PATH",
 ]

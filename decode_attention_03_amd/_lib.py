@@ -25,7 +25,8 @@ _STATUS_NAMES = {
 
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_verify", "mla_split",
-           "mla_merge", "mla_status_string", "mla_last_hip_error")
+           "mla_merge", "mla_kv_append", "mla_kv_dynamic_scale", "mla_status_string",
+           "mla_last_hip_error")
 
 
 class MLAError(RuntimeError):
@@ -74,6 +75,10 @@ def load(path=None):
     lib.mla_split.restype = i32
     lib.mla_merge.argtypes = [vp, vp, i32, ctypes.c_int64, vp, vp, vp]
     lib.mla_merge.restype = i32
+    lib.mla_kv_append.argtypes = [pp, vp, vp, vp, vp, f32, vp]
+    lib.mla_kv_append.restype = i32
+    lib.mla_kv_dynamic_scale.argtypes = [vp, ctypes.c_int64, vp, vp]
+    lib.mla_kv_dynamic_scale.restype = i32
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_hip_error.argtypes = []
@@ -216,3 +221,45 @@ def merge(part_out, part_lse, out=None, lse=None):
     _check(lib.mla_merge(part_out.data_ptr(), part_lse.data_ptr(), S, rows, out.data_ptr(),
                          lse.data_ptr(), _stream(part_out.device)))
     return out, lse
+
+
+def kv_append(kv_new, kv_cache, page_table, seq_lens, kv_scale=1.0):
+    """mla_kv_append: kv_new bf16 [B, Q, 576] into kv_cache (bf16 or FP8 bytes) in place."""
+    lib = load()
+    dev = kv_new.device
+    if dev.type != "cuda":
+        raise MLAError(2, "kv_new must be a GPU tensor")
+    for name, t in (("kv_cache", kv_cache), ("page_table", page_table), ("seq_lens", seq_lens)):
+        if t.device != dev:
+            raise MLAError(2, f"{name} is on {t.device}, kv_new on {dev}")
+    if kv_new.dtype != torch.bfloat16 or kv_new.dim() != 3 or kv_new.shape[2] != LATENT_DIM \
+            or not kv_new.is_contiguous():
+        raise MLAError(2, "kv_new must be contiguous bf16 [B, Q, 576]")
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (16, LATENT_DIM) or not kv_cache.is_contiguous():
+        raise MLAError(2, "kv_cache must be contiguous [num_blocks, 16, 576]")
+    B, Q = kv_new.shape[0], kv_new.shape[1]
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B \
+            or not page_table.is_contiguous():
+        raise MLAError(2, "page_table must be contiguous int32 [B, max_blocks_per_seq]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+        raise MLAError(2, "seq_lens must be contiguous int32 [B]")
+    p = Params(batch=B, num_q_tokens=Q, num_heads=1, num_blocks=kv_cache.shape[0],
+               max_blocks_per_seq=page_table.shape[1], max_seq_len_hint=0,
+               kv_dtype=_kv_dtype(kv_cache), num_splits=0)
+    _check(lib.mla_kv_append(ctypes.byref(p), kv_new.data_ptr(), kv_cache.data_ptr(),
+                             page_table.data_ptr(), seq_lens.data_ptr(), float(kv_scale),
+                             _stream(dev)))
+    return kv_cache
+
+
+def kv_dynamic_scale(x, scale=None):
+    """mla_kv_dynamic_scale over every value of the bf16 tensor x -> float32 [1] on x's device."""
+    lib = load()
+    if x.device.type != "cuda" or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise MLAError(2, "x must be a contiguous bf16 GPU tensor")
+    if scale is None:
+        scale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    if scale.dtype != torch.float32 or scale.device != x.device or scale.numel() < 1:
+        raise MLAError(2, "scale must be a float32 tensor on x's device")
+    _check(lib.mla_kv_dynamic_scale(x.data_ptr(), x.numel(), scale.data_ptr(), _stream(x.device)))
+    return scale

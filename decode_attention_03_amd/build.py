@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmla_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_api.cpp"]
+SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip", "mla_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

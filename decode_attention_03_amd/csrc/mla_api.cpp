@@ -198,6 +198,38 @@ mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_s
   return hip_status(mla::launch_merge(m, (hipStream_t)stream));
 }
 
+mla_status mla_kv_append(const mla_params* p, const void* kv_new, void* kv_cache,
+                         const int32_t* page_table, const int32_t* seq_lens, float kv_scale,
+                         void* stream) {
+  if (!p) return MLA_ERR_NULL_ARG;
+  if (p->batch < 1 || p->batch > 65535) return MLA_ERR_BAD_SHAPE;
+  if (p->num_q_tokens < 1 || p->num_q_tokens > mla::kMaxQ) return MLA_ERR_BAD_SHAPE;
+  if (p->num_blocks < 1 || p->max_blocks_per_seq < 1) return MLA_ERR_BAD_SHAPE;
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_BAD_DTYPE;
+  if (!kv_new || !kv_cache || !page_table || !seq_lens) return MLA_ERR_NULL_ARG;
+  if (((uintptr_t)kv_new | (uintptr_t)kv_cache) & 15) return MLA_ERR_BAD_SHAPE;   // 16-byte rows
+  const bool fp8 = p->kv_dtype == MLA_KV_FP8_E4M3;
+  if (fp8 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_BAD_SCALE;
+  mla::AppendArgs a{};
+  a.kv_new = (const uint16_t*)kv_new;
+  a.kv = (uint8_t*)kv_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.batch = p->batch;
+  a.num_q = p->num_q_tokens;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.kv_scale = fp8 ? kv_scale : 1.f;
+  return hip_status(mla::launch_append(a, fp8, (hipStream_t)stream));
+}
+
+mla_status mla_kv_dynamic_scale(const void* x, int64_t count, float* scale, void* stream) {
+  if (!x || !scale) return MLA_ERR_NULL_ARG;
+  if (count < 0 || count > ((int64_t)1 << 40)) return MLA_ERR_BAD_SHAPE;
+  if ((uintptr_t)scale & 3) return MLA_ERR_BAD_SHAPE;
+  return hip_status(mla::launch_dynamic_scale((const uint16_t*)x, count, scale, (hipStream_t)stream));
+}
+
 const char* mla_status_string(int32_t status) {
   switch (status) {
     case MLA_OK: return "ok";

@@ -53,9 +53,23 @@ struct MergeArgs {
   int32_t num_splits;
 };
 
+struct AppendArgs {
+  const uint16_t* kv_new;     // bf16 [B][Q][576]
+  uint8_t* kv;                // bf16 or fp8 [NB][16][576]
+  const int32_t* page_table;  // [B][max_blocks]
+  const int32_t* seq_lens;    // [B]
+  int32_t batch;
+  int32_t num_q;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  float kv_scale;             // fp8 only
+};
+
 // Host launchers (defined next to their kernels).  Return hipSuccess or the
 // launch error.
 hipError_t launch_split(const SplitArgs& a, bool fp8, bool final_out, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_dynamic_scale(const uint16_t* x, int64_t count, float* scale, hipStream_t stream);
 
 }  // namespace mla

@@ -153,6 +153,39 @@ mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
 mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_splits,
                      int64_t rows, void* out, float* lse, void* stream);
 
+/* KV-cache append: write the latents of the Q newest positions of every
+ * sequence into their cache slots, the step before attention in a decode or
+ * verify step.  An FP8 cache stores one byte per value under a per-tensor
+ * scale ("Kimi K2.6 + DFlash on 8x MI300X (508 tok/s)", section "st=2 vs
+ * st=8 & FP8 vs BF16": FP8 doubles the cache's token capacity; section
+ * "Next": auto-computed scales today, static calibration proposed).
+ *   kv_new  bf16 [batch][num_q_tokens][576], 16-byte aligned
+ *   kv_cache bf16 or FP8 E4M3FN bytes [num_blocks][16][576], 16-byte aligned
+ * New token j of sequence b goes to position t = seq_lens[b] - Q + j (seq_lens
+ * count the new tokens, as in mla_verify): block page_table[b][t / 16], row
+ * t % 16.  bf16 cache: the bits are copied.  FP8 cache: each value x becomes
+ * the E4M3FN code nearest to the float32 quotient x / kv_scale (IEEE
+ * division; ties to even; |x / kv_scale| >= 448 saturates to +-448); inputs
+ * must be finite.  Uses p->batch, num_q_tokens (1..8), num_blocks,
+ * max_blocks_per_seq and kv_dtype; the other fields are ignored.  A slot
+ * with t < 0, t / 16 >= max_blocks_per_seq or a page-table entry outside
+ * [0, num_blocks) is a caller error and is skipped (nothing is written).
+ * Errors: NULL_ARG, BAD_SHAPE (ranges, alignment), BAD_DTYPE, BAD_SCALE
+ * (FP8 with kv_scale not finite and positive), HIP. */
+mla_status mla_kv_append(const mla_params* p, const void* kv_new, void* kv_cache,
+                         const int32_t* page_table, const int32_t* seq_lens, float kv_scale,
+                         void* stream);
+
+/* Dynamic per-tensor FP8 scale of `count` bf16 values x (the auto-computed
+ * scale of the same page, section "Next"): writes, to the device float
+ * *scale (4-byte aligned), fp32(max|x| / 448) -- 1.0 when every value is
+ * zero or count == 0, +inf when the largest magnitude is inf, NaN when a
+ * value is NaN.  The maximum is exact (taken over bf16 magnitudes); the
+ * division is IEEE float32.  Three small kernels on `stream`; *scale doubles
+ * as their accumulator, so it must not be read by other work until they end.
+ * Errors: NULL_ARG, BAD_SHAPE (count < 0 or > 2^40, misaligned scale), HIP. */
+mla_status mla_kv_dynamic_scale(const void* x, int64_t count, float* scale, void* stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(int32_t status);
 

@@ -141,3 +141,29 @@ def test_split_and_merge_validation(lib):
     assert lib.mla_merge(FAKE, FAKE, 4097, 10, FAKE, FAKE, None) == SHAPE
     assert lib.mla_merge(FAKE, FAKE, 4, 0, FAKE, FAKE, None) == SHAPE
     assert lib.mla_merge(FAKE, FAKE, 4, (1 << 28) + 1, FAKE, FAKE, None) == SHAPE
+
+
+def test_append_and_scale_validation(lib):
+    p = params(num_heads=0, num_splits=-5)     # fields append ignores
+    pb = ctypes.byref(p)
+    A = lib.mla_kv_append
+    assert A(None, FAKE, FAKE, FAKE, FAKE, 0.03, None) == NULL
+    for i in range(4):
+        args = [FAKE] * 4
+        args[i] = None
+        assert A(pb, *args, 0.03, None) == NULL, i
+    for bad in (dict(batch=0), dict(num_q_tokens=0), dict(num_q_tokens=9), dict(num_blocks=0),
+                dict(max_blocks_per_seq=0)):
+        assert A(ctypes.byref(params(**bad)), FAKE, FAKE, FAKE, FAKE, 0.03, None) == SHAPE, bad
+    assert A(ctypes.byref(params(kv_dtype=2)), FAKE, FAKE, FAKE, FAKE, 0.03, None) == DTYPE
+    # 16-byte alignment of the new latents and of the cache
+    assert A(pb, ctypes.c_void_p(0x1008), FAKE, FAKE, FAKE, 0.03, None) == SHAPE
+    assert A(pb, FAKE, ctypes.c_void_p(0x1004), FAKE, FAKE, 0.03, None) == SHAPE
+    for ks in (0.0, -1.0, float("nan"), float("inf")):
+        assert A(pb, FAKE, FAKE, FAKE, FAKE, ks, None) == SCALE, ks
+    D = lib.mla_kv_dynamic_scale
+    assert D(None, 10, FAKE, None) == NULL
+    assert D(FAKE, 10, None, None) == NULL
+    assert D(FAKE, -1, FAKE, None) == SHAPE
+    assert D(FAKE, (1 << 40) + 1, FAKE, None) == SHAPE
+    assert D(FAKE, 10, ctypes.c_void_p(0x1002), None) == SHAPE
