@@ -901,16 +901,22 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB), 0, bytes, kBufferRsrcWord3);
     uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + v4 * G::kPageB;
-    // per-lane source offsets, recomputed here rather than held in registers
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    // LDS slot s = 64c + lane of the page holds source chunk
+    // 36 row + (x ^ swz(row)) with row = s / 36, x = s % 36.  As 36 is a
+    // multiple of 4 the XOR only touches the two low bits, so the source chunk
+    // is s ^ swz(s / 36) = s ^ (s / 144), and s / 144 = d0 + (lane >= t) with
+    // d0 = 64c / 144 and t = 144 (d0 + 1) - 64c known per load: one or three
+    // VALU operations per load instead of a division.
+    static_assert(G::kChunksPerRow == 36, "FP8 page rows of 36 chunks");
+    const uint32_t vb = 16u * (uint32_t)lane;
 #pragma unroll
     for (int c = 0; c < kWaveLoads; ++c) {
-      const uint32_t slot = 64 * c + ln;
-      const uint32_t row = slot / G::kChunksPerRow;
-      const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16,
-                                               row * G::kRowB + x * 16, 0, 0, 0);
+      constexpr int kRowsPerSwz = 4 * G::kChunksPerRow;   // 144 slots per swizzle value
+      const int d0 = (64 * c) / kRowsPerSwz;
+      const int t = kRowsPerSwz * (d0 + 1) - 64 * c;
+      const uint32_t d = (uint32_t)d0 + ((t < 64 && lane >= t) ? 1u : 0u);
+      const uint32_t voff = (vb + 1024u * (uint32_t)c) ^ (d << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16, voff, 0, 0, 0);
     }
   };
 
@@ -1031,17 +1037,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       s = mfma_f8(ka, q1[4], s);
       s = mfma_f8(ka, q2[4], s);
     }
-    // elements 8..15 belong to the partner wave; elements 0..7 stay for softmax
-    xbuf[w][0][lane] = f32x4{s[8], s[9], s[10], s[11]};
-    xbuf[w][1][lane] = f32x4{s[12], s[13], s[14], s[15]};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = s[k];
-    // value operand for the PV of this tile (read now: the tile is not read
-    // after this phase).  Column tile ct, positions 32h + 8e .. +7: source lane
-    // sl of a 16-lane group reads position 32h + 8e + sl/2, i.e. page 2h + e/2,
-    // row 8(e%2) + sl/2, byte half sl%2 of chunk 8v + 2ct + (g16%2),
-    // XOR-swizzled by (row/4)%4 = sl/8 + 2(e%2); vbase is the lane part of that
-    // address and pv_voff(ct, e) the rest.
+    // Value operand for the PV of this tile (read now: the tile is not read
+    // after this phase), issued while the last score MFMAs drain.  Column tile
+    // ct, positions 32h + 8e .. +7: source lane sl of a 16-lane group reads
+    // position 32h + 8e + sl/2, i.e. page 2h + e/2, row 8(e%2) + sl/2, byte
+    // half sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by (row/4)%4 =
+    // sl/8 + 2(e%2); vbase is the lane part of that address and pv_voff(ct, e)
+    // the rest.
+    __builtin_amdgcn_sched_barrier(0);
     {
       u32x2 vr[16];
       read_v128_f8((uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + vbase), vr);
@@ -1051,6 +1054,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
                                                   vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
                                                   vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // elements 8..15 belong to the partner wave; elements 0..7 stay for softmax
+    xbuf[w][0][lane] = f32x4{s[8], s[9], s[10], s[11]};
+    xbuf[w][1][lane] = f32x4{s[12], s[13], s[14], s[15]};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = s[k];
   };
 
   // probabilities p * 2^kPShift against the reference maximum, as two FP8 terms
@@ -1177,16 +1186,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     lds_barrier();
     if (copier) {
       const int it = hs >> 1;
-      int cur;
-      if (it & 1) {
-        cur = ptB;
-        ptB = pt_load(it + 4);
-      } else {
-        cur = ptA;
-        ptA = pt_load(it + 4);
-      }
+      const int cur = (it & 1) ? ptB : ptA;
+      const int nxt = pt_load(it + 4);
       asm volatile("" ::: "memory");   // keep PT(it + 4) ahead of the copies
       issue_tile(it + 2, cur);
+      // use the new entry only after the copies are issued: waiting for it
+      // then leaves them in flight
+      __builtin_amdgcn_sched_barrier(0);
+      if (it & 1) ptB = nxt;
+      else ptA = nxt;
     }
     const float row_sum = hs >= 2 ? check(hs & 1) : 0.f;
     const int st = hs - grp;
