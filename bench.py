@@ -330,15 +330,26 @@ def _rank_merge(mla, first, dev, warmup, steps):
                   pl.view(ranks, first.batch, first.num_q, 12), out=out, lse=lse)
 
     per_graph = 20
+    us = _graph_us(run, dev, warmup, steps, per_graph)
+    nbytes = ranks * rows * (512 * 4 + 4) + rows * (512 * 2 + 4)
+    return {"partials": ranks, "rows": rows, "us": round(us, 3),
+            "gb_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "note": f"seeded partials; HIP graph of {per_graph} merges replayed, HIP events"}
+
+
+def _graph_us(fn, dev, warmup, steps, per_graph=20):
+    """Average duration of fn's kernels: a HIP graph of per_graph calls replayed,
+    HIP events on the launch stream."""
+    import torch
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(stream):
-        run()
+        fn()
     torch.cuda.current_stream(dev).wait_stream(stream)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for _ in range(per_graph):
-            run()
+            fn()
     for _ in range(warmup):
         graph.replay()
     cur = torch.cuda.current_stream(dev)
@@ -349,11 +360,29 @@ def _rank_merge(mla, first, dev, warmup, steps):
         graph.replay()
     e1.record(cur)
     e1.synchronize()
-    us = e0.elapsed_time(e1) / (n * per_graph) * 1e3
-    nbytes = ranks * rows * (512 * 4 + 4) + rows * (512 * 2 + 4)
-    return {"partials": ranks, "rows": rows, "us": round(us, 3),
-            "gb_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "note": f"seeded partials; HIP graph of {per_graph} merges replayed, HIP events"}
+    return e0.elapsed_time(e1) / (n * per_graph) * 1e3
+
+
+def _append_leg(mla, first, dev, warmup, steps):
+    """The step before attention: the Q new latents of every sequence written
+    into their cache slots (quantised for an FP8 cache), and the dynamic
+    per-tensor scale of those latents.  Runs on a copy of the first cache."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(707)
+    new = (torch.randn((first.batch, first.num_q, 576), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    kv = first.kv.clone()
+    scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    ap_us = _graph_us(lambda: mla.kv_append(new, kv, first.page_table, first.seq_lens,
+                                            kv_scale=first.kv_scale), dev, warmup, steps)
+    sc_us = _graph_us(lambda: mla.kv_dynamic_scale(new, scale), dev, warmup, steps)
+    elem = 1 if first.kv_dtype == "fp8" else 2
+    nbytes = new.numel() * 2 + new.numel() * elem + first.batch * 4 * 2
+    del kv
+    return {"rows": first.batch * first.num_q, "append_us": round(ap_us, 3),
+            "append_gb_per_s": round(nbytes / (ap_us * 1e-6) / 1e9, 2),
+            "dynamic_scale_us": round(sc_us, 3),
+            "note": "mla_kv_append of the step's new latents and mla_kv_dynamic_scale of them; "
+                    "HIP graph of 20 calls replayed, HIP events"}
 
 
 def main():
@@ -566,6 +595,7 @@ def main():
         },
     }
     _log(f"split {split_us:.2f} us, merge {merge_us:.2f} us per launch")
+    line["config"]["kv_append"] = _append_leg(mla, first, dev, args.warmup, args.steps)
     if first.heads > 12 and first.heads % 12 == 0:
         line["config"]["rank_merge"] = _rank_merge(mla, first, dev, args.warmup, args.steps)
     if not args.no_cpu_baseline:

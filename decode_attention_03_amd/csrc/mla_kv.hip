@@ -12,9 +12,10 @@
 // bf16 value x: RNE conversion of the float32 quotient x / kv_scale (IEEE
 // division), clamped to +-448 first so that large values saturate.
 //
-// Both kernels are tiny and HBM/latency bound: one thread per 16-byte chunk
-// (8 values) of a new latent; the scale is a grid-stride max over bf16
-// magnitudes combined with one 32-bit atomic max per workgroup.
+// Both are tiny and HBM/latency bound: one thread per 16-byte chunk (8
+// values) of a new latent; the scale of up to 2^16 values is one workgroup's
+// max, of more a grid-stride max over bf16 magnitudes combined with one
+// 32-bit atomic max per workgroup (three launches).
 #include "mla_common.hpp"
 
 namespace mla {
@@ -92,13 +93,26 @@ __global__ __launch_bounds__(kAppendThreads) void amax_kernel(const uint16_t* x,
   }
 }
 
-__global__ void scale_finalize_kernel(uint32_t* slot) {
-  const uint32_t m = *slot;
-  float s;
-  if (m > 0x7F80u) s = __builtin_nanf("");          // a NaN among the values
-  else if (m == 0u) s = 1.f;                         // all zero
-  else s = __uint_as_float(m << 16) / kE4M3Max;      // inf stays inf
-  *(float*)slot = s;
+__device__ __forceinline__ float scale_of(uint32_t m) {
+  if (m > 0x7F80u) return __builtin_nanf("");        // a NaN among the values
+  if (m == 0u) return 1.f;                           // all zero
+  return __uint_as_float(m << 16) / kE4M3Max;        // inf stays inf
+}
+
+__global__ void scale_finalize_kernel(uint32_t* slot) { *(float*)slot = scale_of(*slot); }
+
+// Few values (the new latents of one step): one workgroup, one launch.
+constexpr int64_t kSmallScaleCount = 1 << 16;
+__global__ __launch_bounds__(kAppendThreads) void small_scale_kernel(const uint16_t* x, int64_t count,
+                                                                      float* scale) {
+  __shared__ uint32_t red[kAppendThreads / 64];
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < count; i += kAppendThreads) m = max(m, (uint32_t)(x[i] & 0x7FFFu));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) *scale = scale_of(max(max(red[0], red[1]), max(red[2], red[3])));
 }
 
 }  // namespace
@@ -114,6 +128,10 @@ hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream) {
 }
 
 hipError_t launch_dynamic_scale(const uint16_t* x, int64_t count, float* scale, hipStream_t stream) {
+  if (count <= kSmallScaleCount) {
+    hipLaunchKernelGGL(small_scale_kernel, dim3(1), dim3(kAppendThreads), 0, stream, x, count, scale);
+    return hipGetLastError();
+  }
   uint32_t* slot = (uint32_t*)scale;
   hipLaunchKernelGGL(scale_init_kernel, dim3(1), dim3(1), 0, stream, slot);
   if (count > 0) {

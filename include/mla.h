@@ -181,8 +181,9 @@ mla_status mla_kv_append(const mla_params* p, const void* kv_new, void* kv_cache
  * *scale (4-byte aligned), fp32(max|x| / 448) -- 1.0 when every value is
  * zero or count == 0, +inf when the largest magnitude is inf, NaN when a
  * value is NaN.  The maximum is exact (taken over bf16 magnitudes); the
- * division is IEEE float32.  Three small kernels on `stream`; *scale doubles
- * as their accumulator, so it must not be read by other work until they end.
+ * division is IEEE float32.  One kernel on `stream` for count <= 65536; above
+ * that three small kernels, and *scale doubles as their accumulator, so it
+ * must not be read by other work until they end.
  * Errors: NULL_ARG, BAD_SHAPE (count < 0 or > 2^40, misaligned scale), HIP. */
 mla_status mla_kv_dynamic_scale(const void* x, int64_t count, float* scale, void* stream);
 
