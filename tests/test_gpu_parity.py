@@ -80,6 +80,34 @@ def test_wide_row_blocks(gpu_lib, case):
     compare(out, lse, ro, rl, str(case))
 
 
+@pytest.mark.parametrize("alpha", [0.02, 0.3, 4.0])
+def test_fp8_growing_scores(gpu_lib, alpha):
+    """Queries aligned with one late key, so the running maximum of those rows
+    jumps far above the early tiles' (by a few units up to hundreds in log2
+    units): the reference maximum moves, the probability scale follows it,
+    and for the largest jumps the accumulators are rebased.  The lse bound is
+    the absolute 1e-3 while |lse| stays in the workloads' range (ln n + 0.4);
+    with alpha = 4 it reaches about 415, where the float32 score sums alone
+    are good to about 1e-5 relative, so there the bound scales with |lse|/32."""
+    _say(f"growing scores alpha={alpha}")
+    inp = make_inputs([1000, 3000], 3, 12, "fp8", seed=41, device="cuda")
+    kv = inp.kv.view(torch.float8_e4m3fn).float() * inp.kv_scale
+    q = inp.q.clone()
+    pt = inp.page_table.cpu().numpy()
+    for b, L in enumerate(inp.seq_lens.cpu().numpy().tolist()):
+        t = L - 40                                  # a late position, visible to every token
+        lat = kv[int(pt[b, t // 16]), t % 16]
+        for j in range(3):
+            for hh in range(0, 12, 3):              # every third head follows the key
+                q[b, j, hh] = (alpha * (1 + hh) * lat).to(torch.bfloat16)
+    inp.q = q
+    ro, rl, _ = oracle_out(inp)
+    lse_tol = 1e-3 * max(1.0, float(np.abs(rl).max()) / 32.0)
+    for S in (0, 1, 3):
+        out, lse = run_verify(gpu_lib, inp, num_splits=S)
+        compare(out, lse, ro, rl, f"alpha={alpha} S={S}", lse_tol=lse_tol)
+
+
 def test_c6_dcp8_shaped_sampled(gpu_lib):
     _say("config c6")
     inp = make_config("c6", device="cuda")
