@@ -320,7 +320,7 @@ def _rank_merge(mla, first, dev, warmup, steps):
     ranks = first.heads // 12
     rows = first.batch * first.num_q * 12
     g = torch.Generator(device="cpu").manual_seed(606)
-    po = (torch.randn((ranks, rows * 512), generator=g) * 0.05).to(dev)
+    po = (torch.randn((ranks, rows * 512), generator=g) * 0.05).to(torch.bfloat16).to(dev)
     pl = (torch.randn((ranks, rows), generator=g) + 8.0).to(dev)
     out = torch.empty((first.batch, first.num_q, 12, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((first.batch, first.num_q, 12), dtype=torch.float32, device=dev)
@@ -331,7 +331,7 @@ def _rank_merge(mla, first, dev, warmup, steps):
 
     per_graph = 20
     us = _graph_us(run, dev, warmup, steps, per_graph)
-    nbytes = ranks * rows * (512 * 4 + 4) + rows * (512 * 2 + 4)
+    nbytes = ranks * rows * (512 * 2 + 4) + rows * (512 * 2 + 4)
     return {"partials": ranks, "rows": rows, "us": round(us, 3),
             "gb_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
             "note": f"seeded partials; HIP graph of {per_graph} merges replayed, HIP events"}
@@ -428,7 +428,7 @@ def main():
     # Same kernels, same launch configuration as mla_verify (split kernel, then
     # merge when S > 1), issued as separate calls so each kernel can be timed.
     R = first.batch * first.num_q * first.heads
-    po = torch.empty((S, R * 512), dtype=torch.float32, device=dev)
+    po = torch.empty((S, R * 512), dtype=torch.bfloat16, device=dev)
     pl = torch.empty((S, R), dtype=torch.float32, device=dev)
 
     def split_only():

@@ -181,7 +181,7 @@ def verify(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_s
 
 def split(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
           max_seq_len_hint=0, part_out=None, part_lse=None):
-    """mla_split: returns (part_out fp32 [S,B,Q,H,512], part_lse fp32 [S,B,Q,H])."""
+    """mla_split: returns (part_out bf16 [S,B,Q,H,512], part_lse fp32 [S,B,Q,H])."""
     lib = load()
     _check_inputs(q, kv_cache, page_table, seq_lens)
     p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
@@ -190,9 +190,14 @@ def split(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_sp
         raise MLAError(2, "invalid parameters")
     B, Q, H, _ = q.shape
     if part_out is None:
-        part_out = torch.empty((S, B, Q, H, VALUE_DIM), dtype=torch.float32, device=q.device)
+        part_out = torch.empty((S, B, Q, H, VALUE_DIM), dtype=torch.bfloat16, device=q.device)
     if part_lse is None:
         part_lse = torch.empty((S, B, Q, H), dtype=torch.float32, device=q.device)
+    if part_out.dtype != torch.bfloat16 or part_lse.dtype != torch.float32 \
+            or not part_out.is_contiguous() or not part_lse.is_contiguous() \
+            or part_out.device != q.device or part_lse.device != q.device:
+        raise MLAError(2, "partials must be contiguous on q's device "
+                          "(part_out bfloat16, part_lse float32)")
     if part_out.numel() < S * B * Q * H * VALUE_DIM or part_lse.numel() < S * B * Q * H:
         raise MLAError(2, "part_out / part_lse too small")
     _check(lib.mla_split(ctypes.byref(p), q.data_ptr(), kv_cache.data_ptr(), page_table.data_ptr(),
@@ -202,15 +207,15 @@ def split(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_sp
 
 
 def merge(part_out, part_lse, out=None, lse=None):
-    """mla_merge over axis 0: part_out fp32 [S, ..., 512], part_lse fp32 [S, ...]."""
+    """mla_merge over axis 0: part_out bf16 [S, ..., 512], part_lse fp32 [S, ...]."""
     lib = load()
     S = part_out.shape[0]
     lead = tuple(part_out.shape[1:-1])
     if part_out.shape[-1] != VALUE_DIM or tuple(part_lse.shape) != (S,) + lead:
         raise MLAError(2, "part_out must be [S, ..., 512] and part_lse [S, ...]")
-    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32 \
+    if part_out.dtype != torch.bfloat16 or part_lse.dtype != torch.float32 \
             or not part_out.is_contiguous() or not part_lse.is_contiguous():
-        raise MLAError(2, "partials must be contiguous float32")
+        raise MLAError(2, "partials must be contiguous (part_out bfloat16, part_lse float32)")
     rows = 1
     for d in lead:
         rows *= int(d)

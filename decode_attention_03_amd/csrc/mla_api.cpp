@@ -71,7 +71,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t partial_bytes(const mla_params* p, int32_t S) {
   const size_t rows = rows_of(p) * (size_t)S;
-  return align256(rows * mla::kValue * sizeof(float)) + align256(rows * sizeof(float));
+  return align256(rows * mla::kValue * sizeof(uint16_t)) + align256(rows * sizeof(float));
 }
 
 mla_status check_scales(float softmax_scale, float kv_scale, int32_t kv_dtype) {
@@ -123,8 +123,8 @@ mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
   const size_t need = partial_bytes(p, S);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   const size_t rows = rows_of(p) * (size_t)S;
-  a.part_out = (float*)ws;
-  a.part_lse = (float*)((char*)ws + align256(rows * mla::kValue * sizeof(float)));
+  a.part_out = (uint16_t*)ws;
+  a.part_lse = (float*)((char*)ws + align256(rows * mla::kValue * sizeof(uint16_t)));
   st = hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, false, s));
   if (st != MLA_OK) return st;
   mla::MergeArgs m{};
@@ -170,7 +170,7 @@ mla_status mla_verify(const mla_params* p, const void* q, const void* kv_cache,
 
 mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens, float softmax_scale,
-                     float kv_scale, float* part_out, float* part_lse, void* stream) {
+                     float kv_scale, void* part_out, float* part_lse, void* stream) {
   mla_status st = check_params(p, mla::kMaxQ);
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !page_table || !seq_lens || !part_out || !part_lse) return MLA_ERR_NULL_ARG;
@@ -178,18 +178,18 @@ mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
   if (st != MLA_OK) return st;
   const int32_t S = choose_splits(p);
   mla::SplitArgs a = make_args(p, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, S);
-  a.part_out = part_out;
+  a.part_out = (uint16_t*)part_out;
   a.part_lse = part_lse;
   return hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, false, (hipStream_t)stream));
 }
 
-mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_splits, int64_t rows,
+mla_status mla_merge(const void* part_out, const float* part_lse, int32_t num_splits, int64_t rows,
                      void* out, float* lse, void* stream) {
   if (!part_out || !part_lse || !out || !lse) return MLA_ERR_NULL_ARG;
   if (num_splits < 1 || num_splits > 4096) return MLA_ERR_BAD_SHAPE;
   if (rows < 1 || rows > ((int64_t)1 << 28)) return MLA_ERR_BAD_SHAPE;   // grid: 4 workgroups per row
   mla::MergeArgs m{};
-  m.part_out = part_out;
+  m.part_out = (const uint16_t*)part_out;
   m.part_lse = part_lse;
   m.out = (uint16_t*)out;
   m.lse = lse;

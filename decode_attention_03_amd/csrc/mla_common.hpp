@@ -31,7 +31,7 @@ struct SplitArgs {
   const uint8_t* kv;          // bf16 or fp8 [NB][16][576]
   const int32_t* page_table;  // [B][max_blocks]
   const int32_t* seq_lens;    // [B]
-  float* part_out;            // fp32 [S][B][Q][H][512]  (partial mode)
+  uint16_t* part_out;         // bf16 [S][B][Q][H][512]  (partial mode)
   float* part_lse;            // fp32 [S][B][Q][H]
   uint16_t* out;              // bf16 [B][Q][H][512]     (final mode, S == 1)
   float* lse;                 // fp32 [B][Q][H]
@@ -45,7 +45,7 @@ struct SplitArgs {
 };
 
 struct MergeArgs {
-  const float* part_out;      // [S][rows][512]
+  const uint16_t* part_out;   // bf16 [S][rows][512]
   const float* part_lse;      // [S][rows]
   uint16_t* out;              // bf16 [rows][512]
   float* lse;                 // [rows]

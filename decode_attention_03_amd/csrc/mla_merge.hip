@@ -8,7 +8,7 @@
 // HBM-bound streaming of S partial rows per output row.  A 256-thread
 // workgroup holds one or more row slices; in each, LANES split lanes x
 // COLS/4 column chunks (4 floats) stream the partials with up to eight
-// independent 16-byte loads in flight per thread:
+// independent 8-byte loads (four bf16 partial values) in flight per thread:
 //   S <= 8:  1 lane,  whole rows, two rows per workgroup
 //   S <= 32: 2 lanes, whole rows, one row per workgroup
 //   S > 32:  8 lanes, 128-column quarters, four workgroups per row
@@ -23,6 +23,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kMergeThreads = 256;
@@ -88,21 +89,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int col = slice * COLS + 4 * chunk;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
   if (live && m != kNegInf) {
-    const float* po = a.part_out + row * kValue + col;
+    const uint16_t* po = a.part_out + row * kValue + col;
     const int64_t stride = a.rows * kValue;
     for (int s0 = lane_s; s0 < S; s0 += LANES * kInFlight) {
-      f32x4 v[kInFlight];
+      u32x2 v[kInFlight];   // four bf16 each
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) {
         const int s = s0 + LANES * u;
-        v[u] = s < S ? *(const f32x4*)(po + s * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[u] = s < S ? *(const u32x2*)(po + s * stride) : u32x2{0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) {
         const int s = s0 + LANES * u;
         const float wgt = s < S ? cf[s] : 0.f;
         // a partial of weight zero (empty split) contributes nothing, whatever it holds
-        if (wgt != 0.f) acc += wgt * v[u];
+        if (wgt != 0.f) {
+          const f32x4 f{__uint_as_float(v[u][0] << 16), __uint_as_float(v[u][0] & 0xFFFF0000u),
+                        __uint_as_float(v[u][1] << 16), __uint_as_float(v[u][1] & 0xFFFF0000u)};
+          acc += wgt * f;
+        }
       }
     }
   }

@@ -587,7 +587,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       *(bf16x4*)(a.out + orow * kValue + col) = ov;
     } else {
       const int64_t prow = (int64_t)split * a.batch * R + orow;
-      *(f32x4*)(a.part_out + prow * kValue + col) = v * sc;
+      bf16x4 pv4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv4[i] = (__bf16)(v[i] * sc);
+      *(bf16x4*)(a.part_out + prow * kValue + col) = pv4;
     }
   };
   auto store_lse = [&](int r, float m_run, float l_run) {
@@ -1228,7 +1231,10 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
           *(bf16x4*)(a.out + orow * kValue + col) = ov;
         } else {
           const int64_t prow = (int64_t)split * a.batch * R + orow;
-          *(f32x4*)(a.part_out + prow * kValue + col) = v * sc;
+          bf16x4 pv4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv4[i] = (__bf16)(v[i] * sc);
+          *(bf16x4*)(a.part_out + prow * kValue + col) = pv4;
         }
       }
     if (v4 == 0 && h == 0) {

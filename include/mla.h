@@ -50,7 +50,7 @@
  *   seq_lens   int32 [batch]
  *   out        bf16  [batch][num_q_tokens][num_heads][512]
  *   lse        fp32  [batch][num_q_tokens][num_heads]   (natural log)
- *   part_out   fp32  [S][batch][num_q_tokens][num_heads][512]
+ *   part_out   bf16  [S][batch][num_q_tokens][num_heads][512]
  *   part_lse   fp32  [S][batch][num_q_tokens][num_heads]
  *
  * Conventions
@@ -133,24 +133,28 @@ mla_status mla_verify(const mla_params* p, const void* q, const void* kv_cache,
                       float softmax_scale, float kv_scale, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Split-KV partials only: S = mla_num_splits(p) partial outputs (fp32,
- * normalised by their own sums, already multiplied by kv_scale) and their
- * natural-log normalisers, in the part_out / part_lse layouts above. */
+/* Split-KV partials only: S = mla_num_splits(p) partial outputs (bf16, RNE of
+ * the fp32 result, normalised by their own sums, already multiplied by
+ * kv_scale) and their fp32 natural-log normalisers, in the part_out /
+ * part_lse layouts above.  Partial rows are bf16 because they are written
+ * and read once per step at every split boundary; their rounding (relative
+ * 2^-9 per element) stays far below the bf16 rounding of the merged output
+ * combined with the FP8 cache quantisation. */
 mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens,
-                     float softmax_scale, float kv_scale, float* part_out, float* part_lse,
+                     float softmax_scale, float kv_scale, void* part_out, float* part_lse,
                      void* stream);
 
 /* Log-sum-exp merge of S partials ("normalisation information" lets shards be
  * weighted correctly, "Inside Kimi K3 optimization", section "1. Cache -- DCP"):
  *     lse[r] = ln sum_s exp(part_lse[s][r])        (-inf partials weigh 0)
  *     out[r][c] = bf16_rne( sum_s exp(part_lse[s][r] - lse[r]) * part_out[s][r][c] )
- * part_out fp32 [num_splits][rows][512], part_lse fp32 [num_splits][rows],
+ * part_out bf16 [num_splits][rows][512], part_lse fp32 [num_splits][rows],
  * out bf16 [rows][512], lse fp32 [rows].  All partials -inf: out 0, lse -inf.
  * 1 <= num_splits <= 4096, 1 <= rows <= 2^28; otherwise MLA_ERR_BAD_SHAPE.  A
  * partial of weight zero (part_lse = -inf) is never used, whatever part_out
  * holds for it. */
-mla_status mla_merge(const float* part_out, const float* part_lse, int32_t num_splits,
+mla_status mla_merge(const void* part_out, const float* part_lse, int32_t num_splits,
                      int64_t rows, void* out, float* lse, void* stream);
 
 /* KV-cache append: write the latents of the Q newest positions of every

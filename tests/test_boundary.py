@@ -78,7 +78,7 @@ def test_split_planning(lib):
     assert lib.mla_num_splits(ctypes.byref(params(num_heads=96))) == 12
     S = 8
     rows = 4 * 3 * 12
-    expect = ((S * rows * 512 * 4 + 255) // 256) * 256 + ((S * rows * 4 + 255) // 256) * 256
+    expect = ((S * rows * 512 * 2 + 255) // 256) * 256 + ((S * rows * 4 + 255) // 256) * 256
     assert lib.mla_workspace_size(ctypes.byref(params(num_splits=S))) == expect
     assert lib.mla_workspace_size(ctypes.byref(params(num_splits=1))) == 0
 

@@ -194,7 +194,7 @@ def test_split_partials_match_oracle(gpu_lib):
             got_l = pl[s, b].cpu().numpy()
             assert np.array_equal(np.isfinite(got_l), fin)
             assert np.abs(got_l[fin] - rl[s, b][fin]).max() <= 1e-3
-            got_o = po[s, b].cpu().numpy()
+            got_o = po[s, b].float().cpu().numpy()   # bf16 partials
             assert np.abs(got_o - ro[s, b]).max() <= 1e-2 * np.abs(ro[s, b]).max() + 1e-30
 
 
@@ -202,15 +202,19 @@ def test_split_partials_match_oracle(gpu_lib):
 def test_merge_matches_oracle(gpu_lib, S):
     rng = np.random.default_rng(3 + S)
     rows = 300
-    po = rng.normal(size=(S, rows, 512)).astype(np.float32)
+    # bf16 partial rows (the split kernel's output type); the oracle merges the
+    # same bf16 values, widened exactly
+    po_bf = torch.from_numpy(rng.normal(size=(S, rows, 512)).astype(np.float32)).bfloat16()
     pl = (rng.normal(size=(S, rows)) * 3).astype(np.float32)
     pl[rng.random(size=(S, rows)) < 0.2] = -np.inf
     pl[:, 7] = -np.inf          # a row with every partial empty
-    po[np.isneginf(pl)] = 0.0
+    empty = torch.from_numpy(np.isneginf(pl))
+    po_bf[empty] = 0.0
+    po = po_bf.float().numpy()
     # partials of weight zero must not be read into the result: poison them
-    po_dev = po.copy()
-    po_dev[np.isneginf(pl)] = np.nan
-    out, lse = gpu_lib.merge(torch.from_numpy(po_dev).cuda(), torch.from_numpy(pl).cuda())
+    po_dev = po_bf.clone()
+    po_dev[empty] = float("nan")
+    out, lse = gpu_lib.merge(po_dev.cuda(), torch.from_numpy(pl).cuda())
     torch.cuda.synchronize()
     ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64))
     fin = np.isfinite(rl)
