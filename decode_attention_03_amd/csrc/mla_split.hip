@@ -769,6 +769,100 @@ __device__ __forceinline__ void read_v_f8(uint32_t vaddr, u32x2 (&r)[4]) {
 constexpr int kF8Waves = 8;
 constexpr int kF8Threads = kF8Waves * 64;
 
+// LDS reads of the start of an MFMA phase, one round trip: the group's four
+// tile maxima and four row sums of row r32 (red_max / red_sum rows are 128
+// bytes apart) and its two probability terms (as read_p32_f8).
+__device__ __forceinline__ void read_phase_f8(uint32_t maddr, uint32_t saddr, uint32_t paddr,
+                                              float (&rm)[4], float (&rs)[4], i32x8 (&pf)[2]) {
+  u32x4 p0, p1, p2, p3;
+  asm volatile(
+      "ds_read_b32 %0, %12\n\t"
+      "ds_read_b32 %1, %12 offset:128\n\t"
+      "ds_read_b32 %2, %12 offset:256\n\t"
+      "ds_read_b32 %3, %12 offset:384\n\t"
+      "ds_read_b32 %4, %13\n\t"
+      "ds_read_b32 %5, %13 offset:128\n\t"
+      "ds_read_b32 %6, %13 offset:256\n\t"
+      "ds_read_b32 %7, %13 offset:384\n\t"
+      "ds_read_b128 %8, %14\n\t"
+      "ds_read_b128 %9, %14 offset:16\n\t"
+      "ds_read_b128 %10, %14 offset:2560\n\t"
+      "ds_read_b128 %11, %14 offset:2576\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(rm[0]), "=&v"(rm[1]), "=&v"(rm[2]), "=&v"(rm[3]), "=&v"(rs[0]), "=&v"(rs[1]),
+        "=&v"(rs[2]), "=&v"(rs[3]), "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
+      : "v"(maddr), "v"(saddr), "v"(paddr));
+  pf[0] = __builtin_bit_cast(i32x8, u32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]});
+  pf[1] = __builtin_bit_cast(i32x8, u32x8{p2[0], p2[1], p2[2], p2[3], p3[0], p3[1], p3[2], p3[3]});
+}
+
+// Key operands of k-steps at OFF and OFF + 64 (as read_k2_f8<OFF>) together
+// with the PV value operand (as read_v128_f8), one round trip.
+template <int OFF>
+__device__ __forceinline__ void read_k2v_f8(uint32_t a0, uint32_t a1, uint32_t vaddr, i32x8& k0,
+                                            i32x8& k1, u32x2 (&v)[16]) {
+  u32x4 x0, x1, x2, x3;
+  asm volatile(
+      "ds_read_b128 %0, %20 offset:%23\n\t"
+      "ds_read_b128 %1, %21 offset:%23\n\t"
+      "ds_read_b128 %2, %20 offset:%24\n\t"
+      "ds_read_b128 %3, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %4, %22\n\t"
+      "ds_read_b64_tr_b8 %5, %22 offset:4640\n\t"
+      "ds_read_b64_tr_b8 %6, %22 offset:9216\n\t"
+      "ds_read_b64_tr_b8 %7, %22 offset:13856\n\t"
+      "ds_read_b64_tr_b8 %8, %22 offset:32\n\t"
+      "ds_read_b64_tr_b8 %9, %22 offset:4608\n\t"
+      "ds_read_b64_tr_b8 %10, %22 offset:9248\n\t"
+      "ds_read_b64_tr_b8 %11, %22 offset:13824\n\t"
+      "ds_read_b64_tr_b8 %12, %22 offset:64\n\t"
+      "ds_read_b64_tr_b8 %13, %22 offset:4704\n\t"
+      "ds_read_b64_tr_b8 %14, %22 offset:9280\n\t"
+      "ds_read_b64_tr_b8 %15, %22 offset:13920\n\t"
+      "ds_read_b64_tr_b8 %16, %22 offset:96\n\t"
+      "ds_read_b64_tr_b8 %17, %22 offset:4672\n\t"
+      "ds_read_b64_tr_b8 %18, %22 offset:9312\n\t"
+      "ds_read_b64_tr_b8 %19, %22 offset:13888\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]),
+        "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]),
+        "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(a0), "v"(a1), "v"(vaddr), "i"(OFF), "i"(OFF + 64));
+  k0 = __builtin_bit_cast(i32x8, u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+  k1 = __builtin_bit_cast(i32x8, u32x8{x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]});
+}
+
+// Key operand of the k-step at OFF (as read_k_f8<OFF>) with the PV value operand.
+template <int OFF>
+__device__ __forceinline__ i32x8 read_kv_f8(uint32_t a0, uint32_t a1, uint32_t vaddr, u32x2 (&v)[16]) {
+  u32x4 x0, x1;
+  asm volatile(
+      "ds_read_b128 %0, %18 offset:%21\n\t"
+      "ds_read_b128 %1, %19 offset:%21\n\t"
+      "ds_read_b64_tr_b8 %2, %20\n\t"
+      "ds_read_b64_tr_b8 %3, %20 offset:4640\n\t"
+      "ds_read_b64_tr_b8 %4, %20 offset:9216\n\t"
+      "ds_read_b64_tr_b8 %5, %20 offset:13856\n\t"
+      "ds_read_b64_tr_b8 %6, %20 offset:32\n\t"
+      "ds_read_b64_tr_b8 %7, %20 offset:4608\n\t"
+      "ds_read_b64_tr_b8 %8, %20 offset:9248\n\t"
+      "ds_read_b64_tr_b8 %9, %20 offset:13824\n\t"
+      "ds_read_b64_tr_b8 %10, %20 offset:64\n\t"
+      "ds_read_b64_tr_b8 %11, %20 offset:4704\n\t"
+      "ds_read_b64_tr_b8 %12, %20 offset:9280\n\t"
+      "ds_read_b64_tr_b8 %13, %20 offset:13920\n\t"
+      "ds_read_b64_tr_b8 %14, %20 offset:96\n\t"
+      "ds_read_b64_tr_b8 %15, %20 offset:4672\n\t"
+      "ds_read_b64_tr_b8 %16, %20 offset:9312\n\t"
+      "ds_read_b64_tr_b8 %17, %20 offset:13888\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]),
+        "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+        "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(a0), "v"(a1), "v"(vaddr), "i"(OFF));
+  return __builtin_bit_cast(i32x8, u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+}
+
 // Value operand of one PV step: column tiles 0..3 (128 columns) x positions
 // 32h + 0..31, sixteen transposed reads at the offsets pv_voff(ct, e).
 static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 9280 &&
@@ -932,33 +1026,35 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   {
     const bool real = myrow < R && ntiles > 0;   // empty splits skip the query work
     const uint16_t* qp = a.q + ((int64_t)b * R + (real ? myrow : 0)) * kLatent + 32 * h;
-    const uint32_t keep = real ? 0xFFFFFFFFu : 0u;
     const int pt0 = pt_load(grp);
     ptA = pt_load(2);
     ptB = pt_load(3);
+    // only real rows are read, and only the k-steps this wave owns: padding
+    // rows and the missing fifth step of dh = 1 stay zero (the query reads of
+    // all workgroups go out at once, so every byte not read shortens them)
     u32x4 qv[5][4];
 #pragma unroll
-    for (int ks = 0; ks < 5; ++ks) {
-      // the fifth step of dh = 1 does not exist: reload step 8 and drop it below
-      const int kk = min(ks0 + ks, 8);
+    for (int ks = 0; ks < 5; ++ks)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qv[ks][c] = *(const u32x4*)(qp + 64 * kk + 8 * c);
+      for (int c = 0; c < 4; ++c) qv[ks][c] = u32x4{0u, 0u, 0u, 0u};
+    if (real) {
+#pragma unroll
+      for (int ks = 0; ks < 5; ++ks)
+        if (ks < nks)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) qv[ks][c] = *(const u32x4*)(qp + 64 * (ks0 + ks) + 8 * c);
     }
     asm volatile("" ::: "memory");   // keep the query loads ahead of the copies
     issue_tile(grp, pt0);
     __builtin_amdgcn_sched_barrier(0);   // and the copies ahead of the query arithmetic
     float mx = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 5; ++ks) {
-      const uint32_t kp = (ks < nks) ? keep : 0u;
+    for (int ks = 0; ks < 5; ++ks)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          qv[ks][c][k] &= kp;
+        for (int k = 0; k < 4; ++k)
           mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(qv[ks][c][k])), fabsf(bf16_hi(qv[ks][c][k]))));
-        }
-    }
     mx = max32(mx);                                 // the two lanes holding this row
     if (h == 0) qmax[w][r32] = mx;
     lds_barrier();
@@ -972,6 +1068,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     q_unscale = pow2f(-e);
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks) {
+      if (ks >= nks) break;   // dh = 1 has four steps
       i32x8 hi8, lo8;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -1012,16 +1109,24 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   uint8_t* const pg_lds = p_lds[grp];
 
   // ---- a4: partial S^T over this wave's k-steps, then the value fragments.
-  auto qk = [&](int T) {
+  // Key addresses of tile T for this wave (lane's row, chunk pair 2h, 2h + 1).
+  auto kaddr = [&](int T, uint32_t& kb0, uint32_t& kb1) {
     const uint8_t* tile = kv_lds + (T % kNBuf) * kTileB;
+    kb0 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h, 0) + 64 * ks0);
+    kb1 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h + 1, 0) + 64 * ks0);
+  };
+  // The value operand for the PV of this tile is read with the
+  // last key operands (the tile is not read after this phase).  Column tile
+  // ct, positions 32h + 8e .. +7: source lane sl of a 16-lane group reads
+  // position 32h + 8e + sl/2, i.e. page 2h + e/2, row 8(e%2) + sl/2, byte half
+  // sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by (row/4)%4 = sl/8 +
+  // 2(e%2); vbase is the lane part of that address and pv_voff(ct, e) the rest.
+  auto qk = [&](int T) {
+    uint32_t kb0, kb1;
+    kaddr(T, kb0, kb1);
+    const uint32_t vaddr = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, kv_lds + (T % kNBuf) * kTileB + vbase);
     f32x16 s = f32x16{};
-    const uint32_t kb0 = (uint32_t)(uintptr_t)LDS_PTR(
-        const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h, 0) + 64 * ks0);
-    const uint32_t kb1 = (uint32_t)(uintptr_t)LDS_PTR(
-        const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h + 1, 0) + 64 * ks0);
-    // the reads of step ks + 1 run while the two MFMAs of step ks execute
-    // k-steps in pairs: one LDS round trip per two steps; the reads of a pair
-    // run while the MFMAs of the previous pair drain
+    u32x2 vr[16];
     i32x8 ka, kb;
     read_k2_f8<0>(kb0, kb1, ka, kb);
     s = mfma_f8(ka, q1[0], s);
@@ -1040,24 +1145,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       s = mfma_f8(ka, q1[4], s);
       s = mfma_f8(ka, q2[4], s);
     }
-    // Value operand for the PV of this tile (read now: the tile is not read
-    // after this phase), issued while the last score MFMAs drain.  Column tile
-    // ct, positions 32h + 8e .. +7: source lane sl of a 16-lane group reads
-    // position 32h + 8e + sl/2, i.e. page 2h + e/2, row 8(e%2) + sl/2, byte
-    // half sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by (row/4)%4 =
-    // sl/8 + 2(e%2); vbase is the lane part of that address and pv_voff(ct, e)
-    // the rest.
     __builtin_amdgcn_sched_barrier(0);
-    {
-      u32x2 vr[16];
-      read_v128_f8((uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + vbase), vr);
+    read_v128_f8(vaddr, vr);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        vfr[ct] = __builtin_bit_cast(i32x8, u32x8{vr[4 * ct][0], vr[4 * ct][1], vr[4 * ct + 1][0],
-                                                  vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
-                                                  vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int ct = 0; ct < 4; ++ct)
+      vfr[ct] = __builtin_bit_cast(i32x8, u32x8{vr[4 * ct][0], vr[4 * ct][1], vr[4 * ct + 1][0],
+                                                vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
+                                                vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
     // elements 8..15 belong to the partner wave; elements 0..7 stay for softmax
     xbuf[w][0][lane] = f32x4{s[8], s[9], s[10], s[11]};
     xbuf[w][1][lane] = f32x4{s[12], s[13], s[14], s[15]};
@@ -1124,43 +1219,55 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 
   // Start of the phase after group gx's softmax: move gx's reference maxima
   // where a tile maximum passed them by more than 2^kSlack, and in that (rare,
-  // workgroup-uniform) case let gx recompute its probabilities.
-  // Returns the group's row sums of that softmax when gx is this wave's group.
-  auto check = [&](int gx) -> float {
+  // workgroup-uniform) case let gx recompute its probabilities.  This is the
+  // other group's side (gx != grp): it only tracks gx's maxima and joins the
+  // two barriers.
+  auto check = [&](int gx) {
     const float nm = fmaxf(fmaxf(red_max[4 * gx][r32], red_max[4 * gx + 1][r32]),
                            fmaxf(red_max[4 * gx + 2][r32], red_max[4 * gx + 3][r32]));
-    auto sums = [&]() {
-      return (red_sum[4 * grp][r32] + red_sum[4 * grp + 1][r32]) +
-             (red_sum[4 * grp + 2][r32] + red_sum[4 * grp + 3][r32]);
-    };
-    float sm = grp == gx ? sums() : 0.f;   // read together with the maxima
     const float mo = gx ? mref1 : mref0;
     const bool ov = nm > mo + kSlack;
     if (__any(ov)) {
       const float mn = ov ? nm : mo;
-      if (grp == gx) {
-        const float alpha = ov ? __builtin_amdgcn_exp2f(mo - mn) : 1.f;
-        l_run *= alpha;
-        o[0] *= alpha;
-        o[1] *= alpha;
-        o[2] *= alpha;
-        o[3] *= alpha;
-      }
       if (gx) mref1 = mn;
       else mref0 = mn;
       lds_barrier();   // every wave has read the maxima (and the first sums)
-      if (grp == gx) probs(mn);
+      lds_barrier();   // gx has recomputed its probabilities
+    }
+  };
+
+  // The same check run by the group that ran that softmax (gx = grp), on the
+  // maxima and sums read with its phase's other LDS data; after a
+  // recomputation the probability terms pf are read again.
+  const uint32_t p_addr = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, pg_lds + r32 * kPRB + 32 * h);
+  auto check_own = [&](const float (&rm)[4], const float (&rs)[4], i32x8 (&pf)[2]) -> float {
+    const float nm = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+    float sm = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    const float mo = grp ? mref1 : mref0;
+    const bool ov = nm > mo + kSlack;
+    if (__any(ov)) {
+      const float mn = ov ? nm : mo;
+      const float alpha = ov ? __builtin_amdgcn_exp2f(mo - mn) : 1.f;
+      l_run *= alpha;
+      o[0] *= alpha;
+      o[1] *= alpha;
+      o[2] *= alpha;
+      o[3] *= alpha;
+      if (grp) mref1 = mn;
+      else mref0 = mn;
       lds_barrier();
-      if (grp == gx) sm = sums();
+      probs(mn);
+      lds_barrier();
+      sm = (red_sum[4 * grp][r32] + red_sum[4 * grp + 1][r32]) +
+           (red_sum[4 * grp + 2][r32] + red_sum[4 * grp + 3][r32]);
+      read_p32_f8(p_addr, pf);
     }
     return sm;
   };
 
   // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127.
-  auto pv = [&](float row_sum) {
+  auto pv = [&](float row_sum, const i32x8 (&pf)[2]) {
     l_run += row_sum;
-    i32x8 pf[2];
-    read_p32_f8((uint32_t)(uintptr_t)LDS_PTR(const uint8_t, pg_lds + r32 * kPRB + 32 * h), pf);
     // written out: a rolled loop here makes the compiler rotate the four
     // accumulators through one register window with moves
     o[0] = mfma_f8(vfr[0], pf[0], o[0]);
@@ -1199,15 +1306,25 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       if (it & 1) ptB = nxt;
       else ptA = nxt;
     }
-    const float row_sum = hs >= 2 ? check(hs & 1) : 0.f;
     const int st = hs - grp;
     if (st >= 0 && (st & 1) == 0) {
+      // MFMA role (grp == hs % 2): one LDS round trip for the check and the
+      // PV's probabilities (stale data where unused)
       const int T = st >> 1;
-      if (T >= 1) pv(row_sum);
+      float rm[4], rs[4];
+      i32x8 pf[2];
+      read_phase_f8((uint32_t)(uintptr_t)LDS_PTR(const float, &red_max[4 * grp][r32]),
+                    (uint32_t)(uintptr_t)LDS_PTR(const float, &red_sum[4 * grp][r32]), p_addr, rm, rs,
+                    pf);
+      const float row_sum = hs >= 2 ? check_own(rm, rs, pf) : 0.f;
+      if (T >= 1) pv(row_sum, pf);
       if (T < ntiles) qk(T);
-    } else if (st >= 1) {
-      const int T = (st - 1) >> 1;
-      if (T < ntiles) softmax(T);
+    } else {
+      if (hs >= 2) check(hs & 1);
+      if (st >= 1) {
+        const int T = (st - 1) >> 1;
+        if (T < ntiles) softmax(T);
+      }
     }
   }
 
