@@ -796,73 +796,6 @@ __device__ __forceinline__ void read_phase_f8(uint32_t maddr, uint32_t saddr, ui
   pf[1] = __builtin_bit_cast(i32x8, u32x8{p2[0], p2[1], p2[2], p2[3], p3[0], p3[1], p3[2], p3[3]});
 }
 
-// Key operands of k-steps at OFF and OFF + 64 (as read_k2_f8<OFF>) together
-// with the PV value operand (as read_v128_f8), one round trip.
-template <int OFF>
-__device__ __forceinline__ void read_k2v_f8(uint32_t a0, uint32_t a1, uint32_t vaddr, i32x8& k0,
-                                            i32x8& k1, u32x2 (&v)[16]) {
-  u32x4 x0, x1, x2, x3;
-  asm volatile(
-      "ds_read_b128 %0, %20 offset:%23\n\t"
-      "ds_read_b128 %1, %21 offset:%23\n\t"
-      "ds_read_b128 %2, %20 offset:%24\n\t"
-      "ds_read_b128 %3, %21 offset:%24\n\t"
-      "ds_read_b64_tr_b8 %4, %22\n\t"
-      "ds_read_b64_tr_b8 %5, %22 offset:4640\n\t"
-      "ds_read_b64_tr_b8 %6, %22 offset:9216\n\t"
-      "ds_read_b64_tr_b8 %7, %22 offset:13856\n\t"
-      "ds_read_b64_tr_b8 %8, %22 offset:32\n\t"
-      "ds_read_b64_tr_b8 %9, %22 offset:4608\n\t"
-      "ds_read_b64_tr_b8 %10, %22 offset:9248\n\t"
-      "ds_read_b64_tr_b8 %11, %22 offset:13824\n\t"
-      "ds_read_b64_tr_b8 %12, %22 offset:64\n\t"
-      "ds_read_b64_tr_b8 %13, %22 offset:4704\n\t"
-      "ds_read_b64_tr_b8 %14, %22 offset:9280\n\t"
-      "ds_read_b64_tr_b8 %15, %22 offset:13920\n\t"
-      "ds_read_b64_tr_b8 %16, %22 offset:96\n\t"
-      "ds_read_b64_tr_b8 %17, %22 offset:4672\n\t"
-      "ds_read_b64_tr_b8 %18, %22 offset:9312\n\t"
-      "ds_read_b64_tr_b8 %19, %22 offset:13888\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]),
-        "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]),
-        "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
-      : "v"(a0), "v"(a1), "v"(vaddr), "i"(OFF), "i"(OFF + 64));
-  k0 = __builtin_bit_cast(i32x8, u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
-  k1 = __builtin_bit_cast(i32x8, u32x8{x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]});
-}
-
-// Key operand of the k-step at OFF (as read_k_f8<OFF>) with the PV value operand.
-template <int OFF>
-__device__ __forceinline__ i32x8 read_kv_f8(uint32_t a0, uint32_t a1, uint32_t vaddr, u32x2 (&v)[16]) {
-  u32x4 x0, x1;
-  asm volatile(
-      "ds_read_b128 %0, %18 offset:%21\n\t"
-      "ds_read_b128 %1, %19 offset:%21\n\t"
-      "ds_read_b64_tr_b8 %2, %20\n\t"
-      "ds_read_b64_tr_b8 %3, %20 offset:4640\n\t"
-      "ds_read_b64_tr_b8 %4, %20 offset:9216\n\t"
-      "ds_read_b64_tr_b8 %5, %20 offset:13856\n\t"
-      "ds_read_b64_tr_b8 %6, %20 offset:32\n\t"
-      "ds_read_b64_tr_b8 %7, %20 offset:4608\n\t"
-      "ds_read_b64_tr_b8 %8, %20 offset:9248\n\t"
-      "ds_read_b64_tr_b8 %9, %20 offset:13824\n\t"
-      "ds_read_b64_tr_b8 %10, %20 offset:64\n\t"
-      "ds_read_b64_tr_b8 %11, %20 offset:4704\n\t"
-      "ds_read_b64_tr_b8 %12, %20 offset:9280\n\t"
-      "ds_read_b64_tr_b8 %13, %20 offset:13920\n\t"
-      "ds_read_b64_tr_b8 %14, %20 offset:96\n\t"
-      "ds_read_b64_tr_b8 %15, %20 offset:4672\n\t"
-      "ds_read_b64_tr_b8 %16, %20 offset:9312\n\t"
-      "ds_read_b64_tr_b8 %17, %20 offset:13888\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]),
-        "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
-        "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
-      : "v"(a0), "v"(a1), "v"(vaddr), "i"(OFF));
-  return __builtin_bit_cast(i32x8, u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
-}
-
 // Value operand of one PV step: column tiles 0..3 (128 columns) x positions
 // 32h + 0..31, sixteen transposed reads at the offsets pv_voff(ct, e).
 static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 9280 &&
@@ -1115,12 +1048,13 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     kb0 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h, 0) + 64 * ks0);
     kb1 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h + 1, 0) + 64 * ks0);
   };
-  // The value operand for the PV of this tile is read with the
-  // last key operands (the tile is not read after this phase).  Column tile
-  // ct, positions 32h + 8e .. +7: source lane sl of a 16-lane group reads
-  // position 32h + 8e + sl/2, i.e. page 2h + e/2, row 8(e%2) + sl/2, byte half
-  // sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by (row/4)%4 = sl/8 +
-  // 2(e%2); vbase is the lane part of that address and pv_voff(ct, e) the rest.
+  // The value operand for the PV of this tile is read after the last key
+  // operands, while the last score MFMAs drain (the tile is not read after
+  // this phase).  Column tile ct, positions 32h + 8e .. +7: source lane sl of
+  // a 16-lane group reads position 32h + 8e + sl/2, i.e. page 2h + e/2, row
+  // 8(e%2) + sl/2, byte half sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by
+  // (row/4)%4 = sl/8 + 2(e%2); vbase is the lane part of that address and
+  // pv_voff(ct, e) the rest.
   auto qk = [&](int T) {
     uint32_t kb0, kb1;
     kaddr(T, kb0, kb1);
