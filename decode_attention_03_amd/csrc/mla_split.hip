@@ -78,6 +78,36 @@ constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// Workgroup -> (split, sequence, query-row block) over a one-dimensional grid.
+// Units u = split + S * sequence in id order, so the splits of one sequence
+// (which read the same query rows) start together on all XCDs.  With several
+// row blocks, which read the same pages, the row blocks of a unit are kept on
+// one XCD back to back: consecutive ids go to the eight XCDs in turn (each
+// with its own L2), so XCD x's k-th id takes row block k % Z of its unit
+// 8 (k / Z) + x; this is a bijection when the unit count is a multiple of 8,
+// else the row block is simply the slowest index.
+struct WgCoord {
+  int split, b, z;
+};
+__device__ __forceinline__ WgCoord wg_coord(int num_splits, int batch, int row_blocks) {
+  const int id = (int)blockIdx.x;
+  const int units = num_splits * batch;
+  int u, z;
+  if (row_blocks > 1 && (units & 7) == 0) {
+    const int k = id >> 3;
+    u = ((k / row_blocks) << 3) + (id & 7);
+    z = k % row_blocks;
+  } else {
+    u = id % units;
+    z = id / units;
+  }
+  WgCoord c;
+  c.split = u % num_splits;
+  c.b = u / num_splits;
+  c.z = z;
+  return c;
+}
+
 // Workgroup barrier for LDS data written with ds_write: drain this wave's LDS
 // traffic, then s_barrier.  (No memory fence: the direct-to-LDS loads are
 // waited for explicitly with vmcnt, so no blanket vmcnt(0) is wanted here.)
@@ -242,10 +272,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int h = lane >> 5;       // 32-lane half
   const int dh = w & 1;          // layout 48: which half of the 576 dims this wave contracts
   const bool t32 = !L16 && w < 2;  // layout 48: wave works on the 32-row tile
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
   const int H = a.heads;
   const int R = a.num_q * H;
+  const WgCoord wc = wg_coord(a.num_splits, a.batch, (R + RPAD - 1) / RPAD);
+  const int split = wc.split;
+  const int b = wc.b;
 
   const int L = a.seq_lens[b];
   const int P = (L + kPage - 1) / kPage;
@@ -262,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int rowA = L16 ? r16 : r32;
   const int rowB = 32 + r16;
   // rows rb0 .. rb0 + RPAD - 1 of the Q*H query rows are this workgroup's
-  const int rb0 = (int)blockIdx.z * RPAD;
+  const int rb0 = wc.z * RPAD;
   const int limA = L - a.num_q + (rb0 + rowA) / H + 1;   // visible: position < lim
   const int limB = L - a.num_q + (rb0 + rowB) / H + 1;
 
@@ -894,10 +925,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int dh = v4 >> 1;
   const int ks0 = dh ? 5 : 0;
   const int nks = dh ? 4 : 5;
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
   const int H = a.heads;
   const int R = a.num_q * H;
+  const WgCoord wc = wg_coord(a.num_splits, a.batch, (R + 63) / 64);
+  const int split = wc.split;
+  const int b = wc.b;
 
   const int L = a.seq_lens[b];
   const int P = (L + kPage - 1) / kPage;
@@ -905,8 +937,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
   const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
 
-  // rows 64 * blockIdx.z .. + 63 of the Q*H query rows are this workgroup's
-  const int myrow = 64 * (int)blockIdx.z + 32 * grp + r32;
+  // rows 64 * wc.z .. + 63 of the Q*H query rows are this workgroup's
+  const int myrow = 64 * wc.z + 32 * grp + r32;
   const int lim = L - a.num_q + myrow / H + 1;   // visible: position < lim
 
   // ---- a2: copies.  Tile T goes to LDS buffer T % 3; wave w copies page
@@ -1301,7 +1333,7 @@ template <int LAYOUT, bool FP8>
 hipError_t launch_layout(const SplitArgs& a, bool final_out, hipStream_t stream) {
   const int rows = a.num_q * a.heads;
   const int rpad = LAYOUT == kLayout16 ? 16 : 48;
-  dim3 grid(a.num_splits, a.batch, (rows + rpad - 1) / rpad);
+  const dim3 grid((unsigned)(a.num_splits * a.batch * ((rows + rpad - 1) / rpad)));
   if (final_out)
     hipLaunchKernelGGL((split_kernel<LAYOUT, FP8, true>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -1313,7 +1345,7 @@ template <bool FP8>
 hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) {
   const int rows = a.num_q * a.heads;
   if (FP8 && rows > 32) {
-    dim3 grid(a.num_splits, a.batch, (rows + 63) / 64);
+    const dim3 grid((unsigned)(a.num_splits * a.batch * ((rows + 63) / 64)));
     if (final_out)
       hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kF8Threads), 0, stream, a);
     else

@@ -65,6 +65,11 @@ WIDE_CASES = [
     ([100], 1, 20, "fp8", 0),
     ([8, 9], 8, 3, "bf16", 0),
     ([33], 7, 16, "fp8", 1),
+    # split x sequence units a multiple of 8 with several row blocks: the row
+    # blocks of a unit are placed on one XCD back to back
+    ([300, 1500], 3, 96, "fp8", 4),
+    ([300, 1500], 3, 96, "bf16", 4),
+    ([257], 1, 128, "fp8", 8),
 ]
 
 
