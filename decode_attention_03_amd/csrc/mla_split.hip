@@ -943,7 +943,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 
   // ---- a2: copies.  Tile T goes to LDS buffer T % 3; wave w copies page
   // w % 4 (nine wave-wide one-KiB loads from one buffer descriptor).  Tiles 0
-  // and 1 are copied in the prologue (waves 0..3 tile 0, waves 4..7 tile 1);
+  // and 1 are copied in the prologue, once the query has arrived (waves 0..3
+  // tile 0, waves 4..7 tile 1);
   // tile T >= 2 is copied by group 1 at E(T - 2), while it runs its softmax,
   // so the copy issue never sits on the MFMA-role path and two tiles are in
   // flight.  A page outside the split, or the positions past seq_len in the
@@ -989,7 +990,9 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   float q_unscale;
   int ptA, ptB;   // group 1: page-table entries of the next two tiles to copy
   {
-    const bool real = myrow < R && ntiles > 0;   // empty splits skip the query work
+    // not conditional on the split being empty: the query reads then wait for
+    // nothing (seq_lens included) and go out first
+    const bool real = myrow < R;
     const uint16_t* qp = a.q + ((int64_t)b * R + (real ? myrow : 0)) * kLatent + 32 * h;
     const int pt0 = pt_load(grp);
     ptA = pt_load(2);
@@ -1009,9 +1012,6 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 #pragma unroll
           for (int c = 0; c < 4; ++c) qv[ks][c] = *(const u32x4*)(qp + 64 * (ks0 + ks) + 8 * c);
     }
-    asm volatile("" ::: "memory");   // keep the query loads ahead of the copies
-    issue_tile(grp, pt0);
-    __builtin_amdgcn_sched_barrier(0);   // and the copies ahead of the query arithmetic
     float mx = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks)
@@ -1020,6 +1020,13 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(qv[ks][c][k])), fabsf(bf16_hi(qv[ks][c][k]))));
+    // The first copies go out once the query has arrived: issued earlier, the
+    // copies of every workgroup (two tiles each) queue ahead of the query reads
+    // and delay them; issued now they land during the query conversion.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    issue_tile(grp, pt0);
+    __builtin_amdgcn_sched_barrier(0);
     mx = max32(mx);                                 // the two lanes holding this row
     if (h == 0) qmax[w][r32] = mx;
     lds_barrier();
@@ -1251,14 +1258,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // T = (hs - g) / 2), odd -> softmax of tile T = (hs - g - 1) / 2.  At each
   // half-step the group that ran its softmax in the previous one (g = hs % 2)
   // is checked first.
-  // Tiles 0 and 1 (the prologue copies) have landed before the loop.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // Tile 0 (group 0's prologue copies) has landed before the loop; tile 1
+  // (group 1's) only before E(1).
+  if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
     const bool copier = grp == 1 && (hs & 1) == 0;
-    // Group 1's vector-memory order: ... PT(T + 2), copies(T), PT(T + 3),
-    // copies(T + 1) ...  Before E(T), T >= 2, copies(T) must have landed
-    // while PT(T + 3) and copies(T + 1) may still be in flight.
-    if (copier && hs >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads + 1));
+    // Group 1's vector-memory order: copies(1), PT(4), copies(2), PT(5),
+    // copies(3) ...  Before E(T), T >= 1, copies(T) must have landed while
+    // PT(T + 3) and copies(T + 1) may still be in flight.
+    if (copier && hs >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads + 1));
     lds_barrier();
     if (copier) {
       const int it = hs >> 1;
@@ -1294,37 +1302,45 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     }
   }
 
-  // no copy may still be writing this workgroup's LDS when it ends
+  // No copy may still be writing this workgroup's LDS when it ends, and the
+  // epilogue reuses the KV buffers: every wave's copies have landed.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  lds_barrier();
 
-  // ---- a7: epilogue (real rows only).  O and l both carry the 2^kPShift factor.
-  if (myrow < R) {
+  // ---- a7: epilogue.  O and l both carry the 2^kPShift factor.  Each wave's
+  // 32 rows x 128 columns go through LDS (the free KV buffers) so that a store
+  // instruction writes four whole 256-byte row segments; stored straight from
+  // the accumulators, each instruction would touch 32 rows with 16 bytes each.
+  {
+    constexpr int kSRow = 256 + 16;   // staged row stride (bytes), skewed against bank conflicts
+    static_assert(kF8Waves * 32 * kSRow <= kNBuf * kTileB, "epilogue staging fits the KV buffers");
+    uint8_t* const stage = kv_lds + w * 32 * kSRow;
     const float sc = l_run > 0.f ? a.out_scale / l_run : 0.f;
-    const int64_t orow = (int64_t)b * R + myrow;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = 128 * v4 + 32 * ct + 8 * q + 4 * h;
-        const f32x4 v{o[ct][4 * q], o[ct][4 * q + 1], o[ct][4 * q + 2], o[ct][4 * q + 3]};
-        if constexpr (FINAL) {
-          bf16x4 ov;
+        bf16x4 ov;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(v[i] * sc);
-          *(bf16x4*)(a.out + orow * kValue + col) = ov;
-        } else {
-          const int64_t prow = (int64_t)split * a.batch * R + orow;
-          bf16x4 pv4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv4[i] = (__bf16)(v[i] * sc);
-          *(bf16x4*)(a.part_out + prow * kValue + col) = pv4;
-        }
+        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[ct][4 * q + i] * sc);
+        *(bf16x4*)(stage + r32 * kSRow + 2 * (32 * ct + 8 * q + 4 * h)) = ov;
       }
-    if (v4 == 0 && h == 0) {
-      const float lv = (l_run > 0.f) ? ((grp ? mref1 : mref0) - kPShift + log2f(l_run)) * kLn2 : kNegInf;
-      if constexpr (FINAL) a.lse[orow] = lv;
-      else a.part_lse[(int64_t)split * a.batch * R + orow] = lv;
+    // each wave reads back only its own rows (LDS is in order within a wave)
+    uint16_t* const dst = FINAL ? a.out : a.part_out;
+    const int64_t row0 = FINAL ? (int64_t)b * R : ((int64_t)split * a.batch + b) * R;
+    const int cc = 8 * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const int grow = 64 * wc.z + 32 * grp + r;
+      const u32x4 v = *(const u32x4*)(stage + r * kSRow + 2 * cc);
+      if (grow < R) *(u32x4*)(dst + (row0 + grow) * kValue + 128 * v4 + cc) = v;
     }
+  }
+  if (myrow < R && v4 == 0 && h == 0) {
+    const float lv = (l_run > 0.f) ? ((grp ? mref1 : mref0) - kPShift + log2f(l_run)) * kLn2 : kNegInf;
+    if constexpr (FINAL) a.lse[(int64_t)b * R + myrow] = lv;
+    else a.part_lse[((int64_t)split * a.batch + b) * R + myrow] = lv;
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
