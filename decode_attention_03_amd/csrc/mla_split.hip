@@ -607,53 +607,60 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     }
   }
 
-  // ---- a7: epilogue (real rows only).
-  const int64_t row_base = (int64_t)b * R + rb0;
-  auto store4 = [&](int r, int col, f32x4 v, float sc) {
-    const int64_t orow = row_base + r;
-    if constexpr (FINAL) {
+  // ---- a7: epilogue.  Each wave's rows x 128 columns go through LDS (the KV
+  // buffers: every copy has landed, and the barrier below ends every wave's
+  // last reads of them), so that a store instruction writes four whole
+  // 256-byte row segments instead of 16 or 32 rows with 16-32 bytes each.
+  lds_barrier();
+  {
+    constexpr int kSRow = 256 + 16;   // staged row stride (bytes), skewed against bank conflicts
+    static_assert(kWaves * RPAD * kSRow <= kNBuf * kTileB, "epilogue staging fits the KV buffers");
+    uint8_t* const stage = kv_lds + w * RPAD * kSRow;
+    auto put4 = [&](int r, int c, f32x4 v, float sc) {
       bf16x4 ov;
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(v[i] * sc);
-      *(bf16x4*)(a.out + orow * kValue + col) = ov;
+      *(bf16x4*)(stage + r * kSRow + 2 * c) = ov;
+    };
+    const float scA = l_runA > 0.f ? a.out_scale / l_runA : 0.f;
+    if constexpr (L16) {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) put4(r16, 16 * ct + 4 * g, o16a[ct], scA);
     } else {
-      const int64_t prow = (int64_t)split * a.batch * R + orow;
-      bf16x4 pv4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv4[i] = (__bf16)(v[i] * sc);
-      *(bf16x4*)(a.part_out + prow * kValue + col) = pv4;
-    }
-  };
-  auto store_lse = [&](int r, float m_run, float l_run) {
-    const float v = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
-    const int64_t orow = row_base + r;
-    if constexpr (FINAL) a.lse[orow] = v;
-    else a.part_lse[(int64_t)split * a.batch * R + orow] = v;
-  };
-  const float scA = l_runA > 0.f ? a.out_scale / l_runA : 0.f;
-  const int col0 = 128 * w;
-  if constexpr (L16) {
-    if (rb0 + r16 < R) {
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) store4(r16, col0 + 16 * ct + 4 * g, o16a[ct], scA);
-      if (w == 0 && g == 0) store_lse(r16, m_runA, l_runA);
-    }
-  } else {
-    if (rb0 + r32 < R) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x4 v{o32[ct][4 * q], o32[ct][4 * q + 1], o32[ct][4 * q + 2], o32[ct][4 * q + 3]};
-          store4(r32, col0 + 32 * ct + 8 * q + 4 * h, v, scA);
+          put4(r32, 32 * ct + 8 * q + 4 * h, v, scA);
         }
-      if (w == 0 && h == 0) store_lse(r32, m_runA, l_runA);
-    }
-    if (rb0 + rowB < R) {
       const float scB = l_runB > 0.f ? a.out_scale / l_runB : 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) store4(rowB, col0 + 16 * ct + 4 * g, o16b[ct], scB);
-      if (w == 0 && g == 0) store_lse(rowB, m_runB, l_runB);
+      for (int ct = 0; ct < 8; ++ct) put4(rowB, 16 * ct + 4 * g, o16b[ct], scB);
+    }
+    // each wave reads back only its own rows (LDS is in order within a wave)
+    uint16_t* const dst = FINAL ? a.out : a.part_out;
+    const int64_t row0 = FINAL ? (int64_t)b * R : ((int64_t)split * a.batch + b) * R;
+    const int cc = 8 * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < RPAD / 4; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const u32x4 v = *(const u32x4*)(stage + r * kSRow + 2 * cc);
+      if (rb0 + r < R) *(u32x4*)(dst + (row0 + rb0 + r) * kValue + 128 * w + cc) = v;
+    }
+  }
+  auto store_lse = [&](int r, float m_run, float l_run) {
+    const float v = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
+    const int64_t lrow = ((FINAL ? 0 : (int64_t)split * a.batch) + b) * R + rb0 + r;
+    if constexpr (FINAL) a.lse[lrow] = v;
+    else a.part_lse[lrow] = v;
+  };
+  if (w == 0) {
+    if constexpr (L16) {
+      if (g == 0 && rb0 + r16 < R) store_lse(r16, m_runA, l_runA);
+    } else {
+      if (h == 0 && rb0 + r32 < R) store_lse(r32, m_runA, l_runA);
+      if (g == 0 && rb0 + rowB < R) store_lse(rowB, m_runB, l_runB);
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
