@@ -707,31 +707,15 @@ constexpr int pv_voff(int ct, int e) {
          16 * (4 * (ct >> 1) + 2 * ((ct ^ e) & 1));
 }
 
-// Four transposed FP8 LDS reads (column tile CT, positions 0..31 of the lane's
-// half) for the PV value operand.  Issued from inline assembly, which waits for
-// its own reads before it ends: the compiler would otherwise treat these reads
-// as possibly aliasing the in-flight direct-to-LDS copies of later tiles and
-// wait for all of them (vmcnt(0)), which defeats the copy pipeline.  The
-// copies of the tile being read were waited for explicitly before the barrier
-// that published it.
-// The two FP8 probability terms of one lane (32 bytes each, 64 * 80 bytes
-// apart), read the same way for the same reason.
-__device__ __forceinline__ void read_p_f8(uint32_t paddr, i32x8 (&pf)[2]) {
-  u32x4 a0, a1, b0, b1;
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:16\n\t"
-      "ds_read_b128 %2, %4 offset:5120\n\t"
-      "ds_read_b128 %3, %4 offset:5136\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
-      : "v"(paddr));
-  pf[0] = __builtin_bit_cast(i32x8, u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-  pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
-}
+// LDS reads of the FP8 kernel's key, value and probability operands are
+// issued from inline assembly, which waits for its own reads before it ends:
+// the compiler would otherwise treat these reads as possibly aliasing the
+// in-flight direct-to-LDS copies of later tiles and wait for all of them
+// (vmcnt(0)), which defeats the copy pipeline.  The copies of the tile being
+// read were waited for explicitly before the barrier that published it.
 
 // Key operand of one k-step: 16 bytes at each of two lane addresses (chunks
-// 4ks + 2h and 4ks + 2h + 1 of the lane's position row), read the same way.
+// 4ks + 2h and 4ks + 2h + 1 of the lane's position row).
 template <int OFF>
 __device__ __forceinline__ i32x8 read_k_f8(uint32_t a0, uint32_t a1) {
   u32x4 v0, v1;
@@ -744,36 +728,10 @@ __device__ __forceinline__ i32x8 read_k_f8(uint32_t a0, uint32_t a1) {
   return __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
 }
 
-// All LDS operands of one PV step in one block: the value operand of column
-// tiles 0 and 1 (four transposed reads each, at pv_voff(ct, e)) and the two
-// probability terms of row tiles 0 and 1 (rows 32t + r32: 80 * 32 bytes apart).
+// Value offsets of column tiles 0 and 1 (read_v128_f8 checks tiles 2 and 3).
 static_assert(pv_voff(0, 0) == 0 && pv_voff(0, 1) == 4640 && pv_voff(0, 2) == 9216 &&
               pv_voff(0, 3) == 13856 && pv_voff(1, 0) == 32 && pv_voff(1, 1) == 4608 &&
-              pv_voff(1, 2) == 9248 && pv_voff(1, 3) == 13824, "offsets in read_pv_f8");
-__device__ __forceinline__ void read_pv_f8(uint32_t vaddr, uint32_t paddr, u32x2 (&v)[8], u32x4 (&p)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b8 %0, %16\n\t"
-      "ds_read_b64_tr_b8 %1, %16 offset:4640\n\t"
-      "ds_read_b64_tr_b8 %2, %16 offset:9216\n\t"
-      "ds_read_b64_tr_b8 %3, %16 offset:13856\n\t"
-      "ds_read_b64_tr_b8 %4, %16 offset:32\n\t"
-      "ds_read_b64_tr_b8 %5, %16 offset:4608\n\t"
-      "ds_read_b64_tr_b8 %6, %16 offset:9248\n\t"
-      "ds_read_b64_tr_b8 %7, %16 offset:13824\n\t"
-      "ds_read_b128 %8, %17\n\t"
-      "ds_read_b128 %9, %17 offset:16\n\t"
-      "ds_read_b128 %10, %17 offset:5120\n\t"
-      "ds_read_b128 %11, %17 offset:5136\n\t"
-      "ds_read_b128 %12, %17 offset:2560\n\t"
-      "ds_read_b128 %13, %17 offset:2576\n\t"
-      "ds_read_b128 %14, %17 offset:7680\n\t"
-      "ds_read_b128 %15, %17 offset:7696\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-        "=&v"(v[7]), "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3]), "=&v"(p[4]), "=&v"(p[5]),
-        "=&v"(p[6]), "=&v"(p[7])
-      : "v"(vaddr), "v"(paddr));
-}
+              pv_voff(1, 2) == 9248 && pv_voff(1, 3) == 13824, "offsets in read_v128_f8");
 
 // Key operands of two consecutive k-steps (offsets OFF and OFF + 64).
 template <int OFF>
@@ -789,19 +747,6 @@ __device__ __forceinline__ void read_k2_f8(uint32_t a0, uint32_t a1, i32x8& k0, 
       : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 64));
   k0 = __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
   k1 = __builtin_bit_cast(i32x8, u32x8{v2[0], v2[1], v2[2], v2[3], v3[0], v3[1], v3[2], v3[3]});
-}
-
-template <int CT>
-__device__ __forceinline__ void read_v_f8(uint32_t vaddr, u32x2 (&r)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b8 %0, %4 offset:%5\n\t"
-      "ds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b8 %2, %4 offset:%7\n\t"
-      "ds_read_b64_tr_b8 %3, %4 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(vaddr), "i"(pv_voff(CT, 0)), "i"(pv_voff(CT, 1)), "i"(pv_voff(CT, 2)),
-        "i"(pv_voff(CT, 3)));
 }
 
 constexpr int kF8Waves = 8;
