@@ -85,6 +85,34 @@ def test_wide_row_blocks(gpu_lib, case):
     compare(out, lse, ro, rl, str(case))
 
 
+@pytest.mark.parametrize("dt,nq,S", [("bf16", 1, 0), ("fp8", 3, 2)])
+def test_max_batch_sampled(gpu_lib, dt, nq, S):
+    """The largest batch the boundary accepts: 65,535 sequences of Q..40
+    positions, so grid and row indexing run at their limits (with S = 2 the
+    merge covers 2.4 M rows).  The oracle checks a seeded sample with both ends."""
+    B = 65535
+    _say(f"max batch {dt} Q={nq} S={S}")
+    lens = np.random.default_rng(65535).integers(nq, 41, size=B)
+    inp = make_inputs(lens, nq, 12, dt, seed=65535 + nq, device="cuda")
+    out, lse = run_verify(gpu_lib, inp, num_splits=S)
+    pick = np.random.default_rng(7).choice(B, size=7, replace=False).tolist()
+    idx = sorted({0, 1, B // 2, B - 2, B - 1} | set(pick))
+    ro, rl, _ = oracle_out(inp, idx)
+    compare(out[idx], lse[idx], ro, rl, f"B={B} {dt} Q={nq} S={S}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_max_splits(gpu_lib, dt):
+    """The largest split count (256): about one page per split of the long
+    sequence, and almost every split of the short ones empty."""
+    _say(f"max splits {dt}")
+    inp = make_inputs([5000, 40, 3], 3, 12, dt, seed=256, device="cuda", spare_blocks=2,
+                      poison=True)
+    out, lse = run_verify(gpu_lib, inp, num_splits=256)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, f"S=256 {dt}")
+
+
 @pytest.mark.parametrize("alpha", [0.02, 0.3, 4.0])
 def test_fp8_growing_scores(gpu_lib, alpha):
     """Queries aligned with one late key, so the running maximum of those rows
