@@ -13,15 +13,18 @@ namespace {
 thread_local int32_t g_last_hip_error = 0;
 
 // Automatic split count.  One split workgroup occupies a CU (its LDS).  A
-// batch of many sequences of unequal length balances better over several
-// rounds of workgroups (up to four rounds over the 256 CUs of an MI355X from
-// 64 sequences on); a few sequences get one full round, since every extra
-// split adds partials to write and merge.  A split keeps at least eight
-// 64-position tiles to amortise its fixed cost (query preparation, first
-// tile, epilogue).
+// split of the longest sequence gets about 1.1 MiB of cache (128 FP8 or 64
+// bf16 pages): less and the fixed cost per workgroup (query preparation,
+// first tiles, epilogue) dominates, more and a batch of unequal lengths
+// balances poorly over the rounds of workgroups.  A batch that would not fill
+// one round of 256 workgroups is split further, while each split keeps at
+// least 32 pages; a count that lands between one and two rounds is cut back
+// to one full round.  (Measured on the workloads: bf16 decode of 32
+// sequences up to 8192 positions runs best at 8 splits, bf16 and FP8 verify
+// of 32 / 64 sequences up to 32768 / 65536 positions at 32, four long
+// sequences at 64.)
 constexpr int kComputeUnits = 256;
-constexpr int kMaxRounds = 4;
-constexpr int kSeqsPerRound = 16;
+constexpr int64_t kSplitBytes = 128 * 16 * 576;   // 1,179,648 bytes of cache per split
 constexpr int kMinPagesPerSplit = 32;
 
 mla_status check_params(const mla_params* p, int max_q) {
@@ -41,19 +44,19 @@ int32_t choose_splits(const mla_params* p) {
   if (p->num_splits > 0) return p->num_splits;
   int64_t max_len = p->max_seq_len_hint > 0 ? p->max_seq_len_hint
                                             : (int64_t)p->max_blocks_per_seq * mla::kPage;
-  int64_t pages = (max_len + mla::kPage - 1) / mla::kPage;
-  int64_t rounds = p->batch / kSeqsPerRound;
-  if (rounds < 1) rounds = 1;
-  if (rounds > kMaxRounds) rounds = kMaxRounds;
+  const int64_t pages = (max_len + mla::kPage - 1) / mla::kPage;
+  const int64_t page_bytes = (int64_t)mla::kPage * mla::kLatent * (p->kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 2);
+  const int64_t pages_per_split = kSplitBytes / page_bytes;   // 128 FP8 or 64 bf16 pages
   // query rows are processed in blocks (64 rows for FP8 verify, else 48 or
   // 16), each a workgroup of its own over the same split
   const int64_t rows = (int64_t)p->num_q_tokens * p->num_heads;
   const int64_t rblock = (p->kv_dtype == MLA_KV_FP8_E4M3 && rows > 32) ? 64 : (rows <= 16 ? 16 : 48);
   const int64_t units = (int64_t)p->batch * ((rows + rblock - 1) / rblock);
-  int64_t s = (rounds * kComputeUnits + units - 1) / units;
-  int64_t cap = pages / kMinPagesPerSplit;
-  if (cap < 1) cap = 1;
-  if (s > cap) s = cap;
+  int64_t s = (pages + pages_per_split - 1) / pages_per_split;
+  int64_t fill = (kComputeUnits + units - 1) / units;
+  const int64_t fill_cap = pages / kMinPagesPerSplit;
+  if (fill > fill_cap) fill = fill_cap;
+  if (s < fill) s = fill;
   // between one and two rounds of workgroups: use exactly one full round
   // rather than leave most CUs idle during a short second one
   const int64_t wg = s * units;

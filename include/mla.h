@@ -107,11 +107,12 @@ typedef struct {
 
 /* Split count the library uses for these parameters (>= 1), or 0 if the
  * parameters are invalid.  Depends only on host-side values: with num_splits
- * = 0 it is min(ceil(256 * R / U), pages / 32), at least 1, for
- * R = clamp(B / 16, 1, 4) rounds of 256 workgroups, U = B times the number of
- * query-row blocks (blocks of 64 rows for FP8 with more than 32 rows Q*H, else
- * 48, or 16 for at most 16 rows) and pages = ceil(hint / 16); when U * S falls
- * between one and two rounds, S = 256 / U (one full round). */
+ * = 0 it is max(ceil(pages / M), min(ceil(256 / U), pages / 32)), at least 1
+ * and at most 256, for pages = ceil(hint / 16), M = 128 pages per split for
+ * FP8 (64 for bf16: about 1.1 MiB of cache either way) and U = B times the
+ * number of query-row blocks (blocks of 64 rows for FP8 with more than 32 rows
+ * Q*H, else 48, or 16 for at most 16 rows); when U * S falls between one and
+ * two rounds of 256 workgroups, S = 256 / U (one full round). */
 int32_t mla_num_splits(const mla_params* p);
 
 /* Bytes of workspace mla_decode / mla_verify need: the partials of all splits

@@ -59,23 +59,33 @@ def test_status_strings(lib):
 
 
 def test_split_planning(lib):
-    # long-context layer: 4 sequences (one round of 256 workgroups) x 2219 pages
-    # -> min(64, 69) = 64 splits
+    # long-context layer, FP8: 4 sequences x 2219 pages -> ceil(2219 / 128) = 18,
+    # but one round of 256 workgroups needs 64 (<= 2219 / 32): 64
     assert lib.mla_num_splits(ctypes.byref(params())) == 64
-    # 4 x 142,000 positions (8875 pages) -> still one round: 64
+    # 4 x 142,000 positions (8875 pages) -> 70 -> 280 workgroups, between one
+    # and two rounds -> one full round: 64
     assert lib.mla_num_splits(ctypes.byref(params(max_seq_len_hint=142000))) == 64
     assert lib.mla_num_splits(ctypes.byref(params(num_splits=8))) == 8
-    # 64 sequences up to 4096 pages -> min(16, 128) = 16 (1024 workgroups)
-    assert lib.mla_num_splits(ctypes.byref(params(batch=64, max_seq_len_hint=65536))) == 16
-    # 32 sequences (two rounds) up to 512 pages -> min(16, 16) = 16
-    assert lib.mla_num_splits(ctypes.byref(params(batch=32, max_seq_len_hint=8192))) == 16
+    # 64 FP8 sequences up to 4096 pages -> 32 (2048 workgroups)
+    assert lib.mla_num_splits(ctypes.byref(params(batch=64, max_seq_len_hint=65536))) == 32
+    # 32 bf16 sequences up to 2048 pages -> 2048 / 64 = 32
+    assert lib.mla_num_splits(ctypes.byref(params(batch=32, max_seq_len_hint=32768,
+                                                  kv_dtype=0))) == 32
+    # 32 bf16 decode sequences (Q = 1) up to 512 pages -> 8 (one round)
+    assert lib.mla_num_splits(ctypes.byref(params(batch=32, num_q_tokens=1,
+                                                  max_seq_len_hint=8192, kv_dtype=0))) == 8
+    # 32 FP8 sequences up to 512 pages -> 4, but one round needs 8 (<= 16): 8
+    assert lib.mla_num_splits(ctypes.byref(params(batch=32, max_seq_len_hint=8192))) == 8
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=256,
                                                   max_blocks_per_seq=16))) == 1
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=20))) == 1
     assert lib.mla_num_splits(ctypes.byref(params(num_heads=129))) == 0
-    # 96 heads x 3 tokens = 288 FP8 rows -> 5 row blocks of 64: 4 x 5 = 20 units
-    # -> min(ceil(256 / 20) = 13, 69) = 13 -> 260 workgroups -> one round: 12
+    # 96 heads x 3 tokens = 288 FP8 rows -> 5 row blocks of 64: 4 x 5 = 20 units;
+    # max(18, min(13, 69)) = 18 -> 360 workgroups -> one round: 12
     assert lib.mla_num_splits(ctypes.byref(params(num_heads=96))) == 12
+    # DCP8 shape: 64 sequences x 5 row blocks up to 512 pages -> 4 (1280 workgroups)
+    assert lib.mla_num_splits(ctypes.byref(params(batch=64, num_heads=96,
+                                                  max_seq_len_hint=8192))) == 4
     S = 8
     rows = 4 * 3 * 12
     expect = ((S * rows * 512 * 2 + 255) // 256) * 256 + ((S * rows * 4 + 255) // 256) * 256
