@@ -824,6 +824,68 @@ __device__ __forceinline__ void read_p32_f8(uint32_t paddr, i32x8 (&pf)[2]) {
   pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
 }
 
+// A lane's query fragments from the block staged in LDS (see the prologue of
+// split_kernel_f8x64): a[c] is the address of chunk pair c at the lane's
+// first k-step, and k-step ks lies 128 ks bytes further.  NKS = 5 or 4 steps.
+template <int NKS>
+__device__ __forceinline__ void read_q_f8(const uint32_t (&a)[4], u32x4 (&v)[5][4]) {
+  static_assert(NKS == 4 || NKS == 5, "four or five k-steps");
+  if constexpr (NKS == 5) {
+    asm volatile(
+        "ds_read_b128 %0, %20\n\t"
+        "ds_read_b128 %1, %21\n\t"
+        "ds_read_b128 %2, %22\n\t"
+        "ds_read_b128 %3, %23\n\t"
+        "ds_read_b128 %4, %20 offset:128\n\t"
+        "ds_read_b128 %5, %21 offset:128\n\t"
+        "ds_read_b128 %6, %22 offset:128\n\t"
+        "ds_read_b128 %7, %23 offset:128\n\t"
+        "ds_read_b128 %8, %20 offset:256\n\t"
+        "ds_read_b128 %9, %21 offset:256\n\t"
+        "ds_read_b128 %10, %22 offset:256\n\t"
+        "ds_read_b128 %11, %23 offset:256\n\t"
+        "ds_read_b128 %12, %20 offset:384\n\t"
+        "ds_read_b128 %13, %21 offset:384\n\t"
+        "ds_read_b128 %14, %22 offset:384\n\t"
+        "ds_read_b128 %15, %23 offset:384\n\t"
+        "ds_read_b128 %16, %20 offset:512\n\t"
+        "ds_read_b128 %17, %21 offset:512\n\t"
+        "ds_read_b128 %18, %22 offset:512\n\t"
+        "ds_read_b128 %19, %23 offset:512\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]),
+          "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[2][0]), "=&v"(v[2][1]),
+          "=&v"(v[2][2]), "=&v"(v[2][3]), "=&v"(v[3][0]), "=&v"(v[3][1]), "=&v"(v[3][2]),
+          "=&v"(v[3][3]), "=&v"(v[4][0]), "=&v"(v[4][1]), "=&v"(v[4][2]), "=&v"(v[4][3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %17\n\t"
+        "ds_read_b128 %2, %18\n\t"
+        "ds_read_b128 %3, %19\n\t"
+        "ds_read_b128 %4, %16 offset:128\n\t"
+        "ds_read_b128 %5, %17 offset:128\n\t"
+        "ds_read_b128 %6, %18 offset:128\n\t"
+        "ds_read_b128 %7, %19 offset:128\n\t"
+        "ds_read_b128 %8, %16 offset:256\n\t"
+        "ds_read_b128 %9, %17 offset:256\n\t"
+        "ds_read_b128 %10, %18 offset:256\n\t"
+        "ds_read_b128 %11, %19 offset:256\n\t"
+        "ds_read_b128 %12, %16 offset:384\n\t"
+        "ds_read_b128 %13, %17 offset:384\n\t"
+        "ds_read_b128 %14, %18 offset:384\n\t"
+        "ds_read_b128 %15, %19 offset:384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]),
+          "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[2][0]), "=&v"(v[2][1]),
+          "=&v"(v[2][2]), "=&v"(v[2][3]), "=&v"(v[3][0]), "=&v"(v[3][1]), "=&v"(v[3][2]),
+          "=&v"(v[3][3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+    v[4][0] = v[4][1] = v[4][2] = v[4][3] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 // Eight waves in two groups of four; group g owns query rows 32g..32g+31 and
 // waves 4g..4g+3, and SIMD k runs wave k of group 0 and wave k of group 1.
 // Within a group, wave v = w & 3:
@@ -882,21 +944,42 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const WgCoord wc = wg_coord(a.num_splits, a.batch, (R + 63) / 64);
   const int split = wc.split;
   const int b = wc.b;
-
-  const int L = a.seq_lens[b];
-  const int P = (L + kPage - 1) / kPage;
-  const int p0 = (int)(((int64_t)split * P) / a.num_splits);
-  const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
-  const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
-
   // rows 64 * wc.z .. + 63 of the Q*H query rows are this workgroup's
   const int myrow = 64 * wc.z + 32 * grp + r32;
+
+  // seq_lens[b] is requested first (a scalar load, waited for below), then
+  // the query block's loads go out: they need only the workgroup's
+  // coordinates (see the query conversion below for the layout).
+  const int L = a.seq_lens[b];
+  uint8_t* const qlds = kv_lds + kTileB;
+  {
+    const int nrows = min(64, R - 64 * wc.z);
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.q + ((int64_t)b * R + 64 * wc.z) * kLatent), 0, nrows * 2 * kLatent, kBufferRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int slot = 64 * (w + 8 * i) + lane;   // 16-byte LDS slot of this lane
+      const int r = slot / 72, x = slot - 72 * (slot / 72);
+      const uint32_t src = 16u * (uint32_t)(72 * r + (x ^ (r & 7)));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, LDS_PTR(void, qlds + 1024 * (w + 8 * i)), 16, src, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int P = (L + kPage - 1) / kPage;
+  // page range [floor(split P / S), floor((split + 1) P / S)) in 32-bit
+  // arithmetic: floor(s P / S) = s floor(P / S) + floor(s (P mod S) / S)
+  const int S = a.num_splits;
+  const int pq = P / S, pr = P - pq * S;
+  const int p0 = split * pq + (split * pr) / S;
+  const int p1 = (split + 1) * pq + ((split + 1) * pr) / S;
+  const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
   const int lim = L - a.num_q + myrow / H + 1;   // visible: position < lim
 
   // ---- a2: copies.  Tile T goes to LDS buffer T % 3; wave w copies page
   // w % 4 (nine wave-wide one-KiB loads from one buffer descriptor).  Tiles 0
-  // and 1 are copied in the prologue, once the query has arrived (waves 0..3
-  // tile 0, waves 4..7 tile 1);
+  // and 1 are copied in the prologue: tile 0 by waves 0..3 as soon as its
+  // page-table entries are known, tile 1 by waves 4..7 once every wave has
+  // read the query staged in buffers 1 and 2;
   // tile T >= 2 is copied by group 1 at E(T - 2), while it runs its softmax,
   // so the copy issue never sits on the MFMA-role path and two tiles are in
   // flight.  A page outside the split, or the positions past seq_len in the
@@ -936,33 +1019,39 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   };
 
   // ---- query: q * 2^e = q1 + q2 (FP8), dims 64(ks0 + ks) + 32h + j of row `myrow`.
-  // The query loads go out before the first copies (vmcnt counts in issue
-  // order), so waiting for them leaves the copies in flight.
+  // The workgroup's 64 query rows (1,152 bytes each) are staged once in KV
+  // buffers 1 and 2 (exactly 73,728 bytes) by direct-to-LDS loads, 16 bytes a
+  // lane: read by every wave straight from memory, the same rows would be
+  // requested twice per workgroup at kernel start, when every workgroup's
+  // first loads queue up.  Rows past Q*H lie outside the buffer range and
+  // arrive as zeros.  Chunk j of row r sits at chunk (j & ~7) | ((j ^ r) & 7)
+  // of its LDS row, so the 16 rows one ds_read_b128 phase reads fall in
+  // distinct bank groups (two-way at most).
   i32x8 q1[5], q2[5];
   float q_unscale;
   int ptA, ptB;   // group 1: page-table entries of the next two tiles to copy
   {
-    // not conditional on the split being empty: the query reads then wait for
-    // nothing (seq_lens included) and go out first
-    const bool real = myrow < R;
-    const uint16_t* qp = a.q + ((int64_t)b * R + (real ? myrow : 0)) * kLatent + 32 * h;
     const int pt0 = pt_load(grp);
     ptA = pt_load(2);
     ptB = pt_load(3);
-    // only real rows are read, and only the k-steps this wave owns: padding
-    // rows and the missing fifth step of dh = 1 stay zero (the query reads of
-    // all workgroups go out at once, so every byte not read shortens them)
+    // tile 0's copies go out as soon as its page-table entries are known
+    // (group 0; buffer 0 is not part of the staged query)
+    if (grp == 0) {
+      issue_tile(0, pt0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));   // this wave's query loads
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    lds_barrier();   // every wave's query loads have landed
     u32x4 qv[5][4];
+    {
+      const int lr = 32 * grp + r32;   // row within the block
+      const uint32_t rb = (uint32_t)(uintptr_t)LDS_PTR(uint8_t, qlds + lr * (2 * kLatent) + 128 * ks0);
+      uint32_t qa[4];
 #pragma unroll
-    for (int ks = 0; ks < 5; ++ks)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qv[ks][c] = u32x4{0u, 0u, 0u, 0u};
-    if (real) {
-#pragma unroll
-      for (int ks = 0; ks < 5; ++ks)
-        if (ks < nks)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) qv[ks][c] = *(const u32x4*)(qp + 64 * (ks0 + ks) + 8 * c);
+      for (int c = 0; c < 4; ++c) qa[c] = rb + 16u * (uint32_t)((4 * h + c) ^ (lr & 7));
+      if (dh) read_q_f8<4>(qa, qv);
+      else read_q_f8<5>(qa, qv);
     }
     float mx = 0.f;
 #pragma unroll
@@ -972,16 +1061,13 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(qv[ks][c][k])), fabsf(bf16_hi(qv[ks][c][k]))));
-    // The first copies go out once the query has arrived: issued earlier, the
-    // copies of every workgroup (two tiles each) queue ahead of the query reads
-    // and delay them; issued now they land during the query conversion.
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    issue_tile(grp, pt0);
-    __builtin_amdgcn_sched_barrier(0);
     mx = max32(mx);                                 // the two lanes holding this row
     if (h == 0) qmax[w][r32] = mx;
-    lds_barrier();
+    lds_barrier();   // also: every wave has read the staged query
+    if (grp == 1) {
+      issue_tile(1, pt0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     mx = fmaxf(qmax[w][r32], qmax[w ^ 2][r32]);     // the other half of the dims
     int e = 0;
     if (mx > 0.f) {
