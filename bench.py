@@ -391,7 +391,7 @@ def main():
         summarize_profiles(*args.summarize_profiles, args.profile_tag)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 

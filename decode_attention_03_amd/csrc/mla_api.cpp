@@ -240,7 +240,7 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_BAD_SHAPE: return "a size is out of range";
     case MLA_ERR_BAD_DTYPE: return "unknown kv_dtype";
     case MLA_ERR_BAD_SCALE: return "softmax_scale not finite, or kv_scale not finite and positive";
-    case MLA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case MLA_ERR_UNSUPPORTED: return "request not supported by this library";
     case MLA_ERR_WORKSPACE: return "workspace missing or smaller than mla_workspace_size()";
     case MLA_ERR_HIP: return "HIP runtime error (see mla_last_hip_error)";
     default: return "unknown status";

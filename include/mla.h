@@ -83,7 +83,7 @@ typedef enum {
   MLA_ERR_BAD_SHAPE = 2,    /* a size is out of range */
   MLA_ERR_BAD_DTYPE = 3,    /* kv_dtype is not an mla_kv_dtype */
   MLA_ERR_BAD_SCALE = 4,    /* softmax_scale not finite, or kv_scale not finite and > 0 */
-  MLA_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  MLA_ERR_UNSUPPORTED = 5,  /* valid request this library does not implement */
   MLA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than mla_workspace_size() */
   MLA_ERR_HIP = 7           /* the HIP runtime reported an error */
 } mla_status;

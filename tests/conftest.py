@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP library, loaded; fails loudly if it is missing on a GPU machine."""
+    """The HIP library, loaded; fails loudly if it is missing on a machine with a GPU."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
