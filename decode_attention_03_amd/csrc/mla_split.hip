@@ -1323,6 +1323,9 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       // MFMA role (grp == hs % 2): one LDS round trip for the check and the
       // PV's probabilities (stale data where unused)
       const int T = st >> 1;
+      // the MFMA role is the phase's critical path: its instructions go first
+      // on the SIMD it shares with a softmax-role wave
+      __builtin_amdgcn_s_setprio(2);
       float rm[4], rs[4];
       i32x8 pf[2];
       read_phase_f8((uint32_t)(uintptr_t)LDS_PTR(const float, &red_max[4 * grp][r32]),
@@ -1331,6 +1334,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       const float row_sum = hs >= 2 ? check_own(rm, rs, pf) : 0.f;
       if (T >= 1) pv(row_sum, pf);
       if (T < ntiles) qk(T);
+      __builtin_amdgcn_s_setprio(0);
     } else {
       if (hs >= 2) check(hs & 1);
       if (st >= 1) {
