@@ -83,7 +83,13 @@ def attend(q_rows, latents, softmax_scale):
 
 
 def _visible(seq_len, num_q, j):
-    """Number of positions query token j may see (causal verify rule)."""
+    """Number of positions query token j may see (causal verify rule).
+
+    The rule needs seq_len >= num_q (the Q new tokens are part of the
+    sequence); a shorter sequence is rejected here rather than given a
+    negative count, which a slice x[:n] would silently wrap around."""
+    if int(seq_len) < int(num_q):
+        raise ValueError(f"seq_len {int(seq_len)} < num_q {int(num_q)}: outside the causal rule")
     return int(seq_len) - int(num_q) + int(j) + 1
 
 

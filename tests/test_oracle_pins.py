@@ -240,6 +240,16 @@ def test_verify_seq_eq_q():
     pin_verify_seq_eq_q()
 
 
+def test_seq_shorter_than_q_rejected():
+    """seq_len < Q is outside the causal rule (the Q new tokens belong to the
+    sequence): the oracle refuses it instead of wrapping a negative count."""
+    assert om._visible(8, 8, 0) == 1
+    with pytest.raises(ValueError):
+        om._visible(5, 8, 0)
+    with pytest.raises(ValueError):
+        om._visible(7, 8, 7)
+
+
 # --------------------------------------------------------------------------- invariants
 
 def _ranges_equal(L, s):
