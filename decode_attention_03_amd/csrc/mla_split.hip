@@ -923,8 +923,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][2 * kPTerm];   // [group][term][row][position]
   __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][2][64];    // partial scores for the partner
-  __shared__ float red_max[kF8Waves][32];
-  __shared__ float red_sum[kF8Waves][32];
+  // tile maxima and row sums of each wave's rows, in one array so that the
+  // two addresses of a row differ by a constant
+  __shared__ float red[2][kF8Waves][32];
+  float (&red_max)[kF8Waves][32] = red[0];
+  float (&red_sum)[kF8Waves][32] = red[1];
   __shared__ float qmax[kF8Waves][32];
 
   const int tid = threadIdx.x;
@@ -973,7 +976,6 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int p0 = split * pq + (split * pr) / S;
   const int p1 = (split + 1) * pq + ((split + 1) * pr) / S;
   const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
-  const int lim = L - a.num_q + myrow / H + 1;   // visible: position < lim
 
   // ---- a2: copies.  Tile T goes to LDS buffer T % 3; wave w copies page
   // w % 4 (nine wave-wide one-KiB loads from one buffer descriptor).  Tiles 0
@@ -1118,6 +1120,24 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int pbase = r32 * kPRB + 32 * sp + 16 * dh + 4 * h;
   uint8_t* const pg_lds = p_lds[grp];
 
+  // An opaque copy of the lane index, taken where a lane-dependent address or
+  // bound is needed inside the loop: derived from it there (one or two VALU
+  // operations), the value does not hold a register of its own across the
+  // loop, where nearly every register is taken.
+  auto lane_now = [&]() -> int {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  // Causal limit of the lane's row (visible: position < lim), needed on edge
+  // tiles only and recomputed there (with an opaque divisor, so that the
+  // division's reciprocal is not kept either).
+  auto lim_now = [&]() -> int {
+    int hd = H;
+    asm volatile("" : "+s"(hd));
+    return L - a.num_q + (64 * wc.z + 32 * grp + (lane_now() & 31)) / hd + 1;
+  };
+
   // ---- a4: partial S^T over this wave's k-steps, then the value fragments.
   // Key addresses of tile T for this wave (lane's row, chunk pair 2h, 2h + 1).
   auto kaddr = [&](int T, uint32_t& kb0, uint32_t& kb1) {
@@ -1165,8 +1185,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
                                                 vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
                                                 vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
     // elements 8..15 belong to the partner wave; elements 0..7 stay for softmax
-    xbuf[w][0][lane] = f32x4{s[8], s[9], s[10], s[11]};
-    xbuf[w][1][lane] = f32x4{s[12], s[13], s[14], s[15]};
+    {
+      const int ln = lane_now();
+      xbuf[w][0][ln] = f32x4{s[8], s[9], s[10], s[11]};
+      xbuf[w][1][ln] = f32x4{s[12], s[13], s[14], s[15]};
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = s[k];
   };
@@ -1197,8 +1220,9 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // 32sp + 16dh + 8(k/4) + 4h + k%4 of the tile.
   auto softmax = [&](int T) {
     {
-      const f32x4 u0 = xbuf[w ^ 2][0][lane];
-      const f32x4 u1 = xbuf[w ^ 2][1][lane];
+      const int ln = lane_now();
+      const f32x4 u0 = xbuf[w ^ 2][0][ln];
+      const f32x4 u1 = xbuf[w ^ 2][1][ln];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         x[k] += u0[k];
@@ -1215,11 +1239,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
         mx = fmaxf(mx, x[k]);
       }
     } else {
+      // position tq = 32 sp + 16 dh + 4 h + (8 (k / 4) + k % 4) is visible
+      // when it is below both tlim and lim - tpos0
+      const int kvis = min(tlim, lim_now() - tpos0) - (32 * sp + 16 * dh + 4 * (lane_now() >> 5));
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int tq = 32 * sp + 16 * dh + 8 * (k >> 2) + 4 * h + (k & 3);
-        const bool ok = tq < tlim && tpos0 + tq < lim;
-        x[k] = ok ? x[k] * cs : kNegInf;
+        x[k] = 8 * (k >> 2) + (k & 3) < kvis ? x[k] * cs : kNegInf;
         mx = fmaxf(mx, x[k]);
       }
     }

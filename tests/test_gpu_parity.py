@@ -85,6 +85,31 @@ def test_wide_row_blocks(gpu_lib, case):
     compare(out, lse, ro, rl, str(case))
 
 
+# FP8 blocks of 33..48 query rows: the eight-wave kernel's second wave group
+# holds 1..16 real rows and the rest padding, at both ends of that range and
+# with every causal token count.
+PARTIAL_GROUP_CASES = [
+    # (seq_lens, Q, H, kv_dtype, num_splits)
+    ([3, 63, 64, 65, 129, 300], 3, 16, "fp8", 0),   # 48 rows
+    ([700, 17], 3, 11, "fp8", 3),                   # 33 rows
+    ([2000, 8], 8, 5, "fp8", 0),                    # 40 rows, eight causal tokens (the
+                                                    # first sees one position)
+    ([4, 16, 100], 4, 12, "fp8", 1),                # 48 rows, direct bf16 output
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_GROUP_CASES, ids=[f"{c[3]}-Q{c[1]}-H{c[2]}-S{c[4]}-{len(c[0])}seq"
+                                                     for c in PARTIAL_GROUP_CASES])
+def test_partial_second_group(gpu_lib, case):
+    lens, nq, nh, dt, S = case
+    _say(f"partial second group {case}")
+    inp = make_inputs(lens, nq, nh, dt, seed=5 * sum(lens) + nq + nh, device="cuda",
+                      spare_blocks=2, poison=True)
+    out, lse = run_verify(gpu_lib, inp, num_splits=S)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, str(case))
+
+
 @pytest.mark.parametrize("dt,nq,S", [("bf16", 1, 0), ("fp8", 3, 2)])
 def test_max_batch_sampled(gpu_lib, dt, nq, S):
     """The largest batch the boundary accepts: 65,535 sequences of Q..40
@@ -210,7 +235,7 @@ def test_c5_long_context_layer(gpu_lib, layer):
 def test_split_partials_match_oracle(gpu_lib):
     """mla_split partials (each split's own normalised output and lse) against the
     oracle's partials over the same page ranges, including empty splits."""
-    lens = [1, 40, 64, 300, 1000]
+    lens = [3, 40, 64, 300, 1000]
     inp = make_inputs(lens, 3, 12, "fp8", seed=77, device="cuda")
     S = 9
     po, pl = gpu_lib.split(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
