@@ -13,7 +13,10 @@
 //   S <= 32: 2 lanes, whole rows, one row per workgroup
 //   S > 32:  8 lanes, 128-column quarters, four workgroups per row
 // Per row slice, the weights exp(lse_s - max) are computed once into LDS
-// (S floats of dynamic LDS per slice), and the lanes are summed in LDS.
+// (S floats of dynamic LDS per slice), and the lanes are summed in LDS.  The
+// first round of partial loads is issued before the lse loads and their
+// reductions (it does not depend on the weights), so the two memory
+// latencies overlap; with S <= 8 LANES that round is all of them.
 #include <math.h>
 
 #include "mla_common.hpp"
@@ -69,34 +72,50 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const bool live = row < a.rows;
   float* cf = coef + rs * S;
 
-  float m = kNegInf;
+  const int chunk = t % kChunks;
+  const int lane_s = t / kChunks;
+  const int col = slice * COLS + 4 * chunk;
+  const uint16_t* const po = a.part_out + (live ? row : (int64_t)0) * kValue + col;
+  const int64_t stride = a.rows * kValue;
+  // lse of split t (the first of this thread's), kept for the weights; issued
+  // first, so that waiting for it leaves the partial loads below in flight
+  // (loads retire from the wait counter in issue order)
+  const int64_t lrow = live ? row : 0;
+  const float ls_t = a.part_lse[(int64_t)min(t, S - 1) * a.rows + lrow];
+  // first round of partial loads (splits lane_s + LANES u), in flight during
+  // the lse reductions.  The loads are unconditional (split index clamped to
+  // S - 1, row 0 for a dead slice: the buffer holds all S x rows partials), so
+  // no branch with its own wait sits between them; a split past S, like an
+  // empty one, has weight zero below and its value is not used.
+  u32x2 v[kInFlight];   // four bf16 each
+#pragma unroll
+  for (int u = 0; u < kInFlight; ++u)
+    v[u] = *(const u32x2*)(po + (int64_t)min(lane_s + LANES * u, S - 1) * stride);
+
+  // (selected only here, after the partial loads have been issued)
+  const float ls0 = (live && t < S) ? ls_t : kNegInf;
+  float m = ls0;
   if (live)
-    for (int s = t; s < S; s += kTPR) m = fmaxf(m, a.part_lse[(int64_t)s * a.rows + row]);
+    for (int s = t + kTPR; s < S; s += kTPR) m = fmaxf(m, a.part_lse[(int64_t)s * a.rows + row]);
   m = slice_reduce<kWPR, true>(m, red);
 
   float wsum = 0.f;
   if (live)
     for (int s = t; s < S; s += kTPR) {
-      const float ls = a.part_lse[(int64_t)s * a.rows + row];
+      const float ls = s == t ? ls0 : a.part_lse[(int64_t)s * a.rows + row];
       const float wgt = (ls == kNegInf) ? 0.f : expf(ls - m);
       cf[s] = wgt;
       wsum += wgt;
     }
   wsum = slice_reduce<kWPR, false>(wsum, red);   // its barriers also publish coef[]
 
-  const int chunk = t % kChunks;
-  const int lane_s = t / kChunks;
-  const int col = slice * COLS + 4 * chunk;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
   if (live && m != kNegInf) {
-    const uint16_t* po = a.part_out + row * kValue + col;
-    const int64_t stride = a.rows * kValue;
     for (int s0 = lane_s; s0 < S; s0 += LANES * kInFlight) {
-      u32x2 v[kInFlight];   // four bf16 each
+      if (s0 != lane_s) {   // later rounds (S > LANES * kInFlight)
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) {
-        const int s = s0 + LANES * u;
-        v[u] = s < S ? *(const u32x2*)(po + s * stride) : u32x2{0u, 0u};
+        for (int u = 0; u < kInFlight; ++u)
+          v[u] = *(const u32x2*)(po + (int64_t)min(s0 + LANES * u, S - 1) * stride);
       }
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) {
