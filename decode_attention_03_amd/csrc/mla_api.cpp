@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "mla.h"
 #include "mla_common.hpp"
 
@@ -18,14 +20,23 @@ thread_local int32_t g_last_hip_error = 0;
 // first tiles, epilogue) dominates, more and a batch of unequal lengths
 // balances poorly over the rounds of workgroups.  A batch that would not fill
 // one round of 256 workgroups is split further, while each split keeps at
-// least 32 pages; a count that lands between one and two rounds is cut back
+// least 2 pages; a count that lands between one and two rounds is cut back
 // to one full round.  (Measured on the workloads: bf16 decode of 32
 // sequences up to 8192 positions runs best at 8 splits, bf16 and FP8 verify
 // of 32 / 64 sequences up to 32768 / 65536 positions at 32, four long
-// sequences at 64.)
+// sequences at 64.  Small batches are latency-bound and gain most from the
+// fill: one 2048-position bf16 sequence runs in 9.9 us at 64 splits against
+// 20.8 us at 4, two of 1024 positions with Q = 3 in 13.4 us at 32 against
+// 42.5 us at 2, one of 256 positions in 9.3 us at 8 against 11.1 us at 1.
+// Beyond 128 splits the merge of the extra partials costs more than the
+// added parallelism gains unless each split keeps 16 pages: one FP8
+// sequence of 8192 positions runs in 18.2 us at 128 splits and 22.9 us at
+// 256, one of 32768 in 24.2 and 24.8 us.)
 constexpr int kComputeUnits = 256;
 constexpr int64_t kSplitBytes = 128 * 16 * 576;   // 1,179,648 bytes of cache per split
-constexpr int kMinPagesPerSplit = 32;
+constexpr int kMinPagesPerSplit = 2;
+constexpr int kWideSplits = 128;        // fill beyond this many splits ...
+constexpr int kMinPagesWide = 16;       // ... only while each keeps this many pages
 
 mla_status check_params(const mla_params* p, int max_q) {
   if (!p) return MLA_ERR_NULL_ARG;
@@ -56,6 +67,7 @@ int32_t choose_splits(const mla_params* p) {
   int64_t fill = (kComputeUnits + units - 1) / units;
   const int64_t fill_cap = pages / kMinPagesPerSplit;
   if (fill > fill_cap) fill = fill_cap;
+  if (fill > kWideSplits) fill = std::max<int64_t>(kWideSplits, std::min<int64_t>(fill, pages / kMinPagesWide));
   if (s < fill) s = fill;
   // between one and two rounds of workgroups: use exactly one full round
   // rather than leave most CUs idle during a short second one

@@ -107,9 +107,10 @@ typedef struct {
 
 /* Split count the library uses for these parameters (>= 1), or 0 if the
  * parameters are invalid.  Depends only on host-side values: with num_splits
- * = 0 it is max(ceil(pages / M), min(ceil(256 / U), pages / 32)), at least 1
- * and at most 256, for pages = ceil(hint / 16), M = 128 pages per split for
- * FP8 (64 for bf16: about 1.1 MiB of cache either way) and U = B times the
+ * = 0 it is max(ceil(pages / M), F), at least 1 and at most 256, with the
+ * fill F = min(ceil(256 / U), pages / 2) and an F above 128 reduced to
+ * max(128, min(F, pages / 16)), for pages = ceil(hint / 16), M = 128 pages
+ * per split for FP8 (64 for bf16: about 1.1 MiB of cache either way) and U = B times the
  * number of query-row blocks (blocks of 64 rows for FP8 with more than 32 rows
  * Q*H, else 48, or 16 for at most 16 rows); when U * S falls between one and
  * two rounds of 256 workgroups, S = 256 / U (one full round). */

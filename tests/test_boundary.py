@@ -74,11 +74,23 @@ def test_split_planning(lib):
     # 32 bf16 decode sequences (Q = 1) up to 512 pages -> 8 (one round)
     assert lib.mla_num_splits(ctypes.byref(params(batch=32, num_q_tokens=1,
                                                   max_seq_len_hint=8192, kv_dtype=0))) == 8
-    # 32 FP8 sequences up to 512 pages -> 4, but one round needs 8 (<= 16): 8
+    # 32 FP8 sequences up to 512 pages -> 4, but one round needs 8 (<= 256): 8
     assert lib.mla_num_splits(ctypes.byref(params(batch=32, max_seq_len_hint=8192))) == 8
+    # one sequence of 16 pages: a round would need 256 splits, 2 pages each
+    # allow 8
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=256,
-                                                  max_blocks_per_seq=16))) == 1
+                                                  max_blocks_per_seq=16))) == 8
+    # 2 bf16 sequences (Q = 3) of 64 pages: 64 / 2 = 32
+    assert lib.mla_num_splits(ctypes.byref(params(batch=2, max_seq_len_hint=1024,
+                                                  kv_dtype=0))) == 32
+    # one FP8 sequence of 512 pages: a round would need 256 splits of 2 pages;
+    # past 128 each split must keep 16 pages -> 128
+    assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=8192))) == 128
+    # 8875 pages: 256 splits keep 34 pages each
+    assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=142000))) == 256
+    # two pages: one split
     assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=20))) == 1
+    assert lib.mla_num_splits(ctypes.byref(params(batch=1, max_seq_len_hint=48))) == 1
     assert lib.mla_num_splits(ctypes.byref(params(num_heads=129))) == 0
     # 96 heads x 3 tokens = 288 FP8 rows -> 5 row blocks of 64: 4 x 5 = 20 units;
     # max(18, min(13, 69)) = 18 -> 360 workgroups -> one round: 12
