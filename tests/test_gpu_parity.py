@@ -110,6 +110,39 @@ def test_partial_second_group(gpu_lib, case):
     compare(out, lse, ro, rl, str(case))
 
 
+def _random_cases(n, seed):
+    # seeded shapes across the kernel choices: query rows Q*H on both sides of
+    # 16, 32, 48 and 64 (layouts and row blocks), Q = 1..8, both KV types,
+    # automatic and forced split counts, ragged lengths >= Q
+    rng = np.random.default_rng(seed)
+    heads = [1, 2, 3, 5, 6, 8, 11, 12, 16, 17, 20, 24, 32, 33, 48, 64, 96, 128]
+    out = []
+    for _ in range(n):
+        nq = int(rng.integers(1, 9))
+        nh = int(rng.choice(heads))
+        nb = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(nq, 2200, size=nb)]
+        dt = str(rng.choice(["bf16", "fp8"]))
+        S = int(rng.choice([0, 0, 1, 2, 5, 16]))
+        out.append((lens, nq, nh, dt, S))
+    return out
+
+
+RANDOM_CASES = _random_cases(24, 2024)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"{i}-{c[3]}-Q{c[1]}-H{c[2]}-S{c[4]}"
+                                                    for i, c in enumerate(RANDOM_CASES)])
+def test_random_shapes(gpu_lib, case):
+    lens, nq, nh, dt, S = case
+    _say(f"random case {case}")
+    inp = make_inputs(lens, nq, nh, dt, seed=11 * sum(lens) + nq + nh, device="cuda",
+                      spare_blocks=1, poison=True)
+    out, lse = run_verify(gpu_lib, inp, num_splits=S)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, str(case))
+
+
 @pytest.mark.parametrize("dt,nq,S", [("bf16", 1, 0), ("fp8", 3, 2)])
 def test_max_batch_sampled(gpu_lib, dt, nq, S):
     """The largest batch the boundary accepts: 65,535 sequences of Q..40
