@@ -113,6 +113,17 @@ mla::SplitArgs make_args(const mla_params* p, const void* q, const void* kv, con
   return a;
 }
 
+// Both launches of a call (split, and merge when S > 1) within the 32-bit
+// grid size of a dispatch.
+bool launches_fit(const mla::SplitArgs& a, const mla_params* p, int32_t S) {
+  if (mla::split_work_items(a, p->kv_dtype == MLA_KV_FP8_E4M3) > mla::kMaxWorkItems) return false;
+  if (S == 1) return true;
+  mla::MergeArgs m{};
+  m.rows = (int64_t)rows_of(p);
+  m.num_splits = S;
+  return mla::merge_work_items(m) <= mla::kMaxWorkItems;
+}
+
 mla_status hip_status(hipError_t e) {
   if (e == hipSuccess) return MLA_OK;
   g_last_hip_error = (int32_t)e;
@@ -130,6 +141,7 @@ mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
   const int32_t S = choose_splits(p);
   hipStream_t s = (hipStream_t)stream;
   mla::SplitArgs a = make_args(p, q, kv, pt, sl, softmax_scale, kv_scale, S);
+  if (!launches_fit(a, p, S)) return MLA_ERR_UNSUPPORTED;
   if (S == 1) {
     a.out = (uint16_t*)out;
     a.lse = lse;
@@ -193,6 +205,8 @@ mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
   if (st != MLA_OK) return st;
   const int32_t S = choose_splits(p);
   mla::SplitArgs a = make_args(p, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, S);
+  if (mla::split_work_items(a, p->kv_dtype == MLA_KV_FP8_E4M3) > mla::kMaxWorkItems)
+    return MLA_ERR_UNSUPPORTED;
   a.part_out = (uint16_t*)part_out;
   a.part_lse = part_lse;
   return hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, false, (hipStream_t)stream));
@@ -202,7 +216,7 @@ mla_status mla_merge(const void* part_out, const float* part_lse, int32_t num_sp
                      void* out, float* lse, void* stream) {
   if (!part_out || !part_lse || !out || !lse) return MLA_ERR_NULL_ARG;
   if (num_splits < 1 || num_splits > 4096) return MLA_ERR_BAD_SHAPE;
-  if (rows < 1 || rows > ((int64_t)1 << 28)) return MLA_ERR_BAD_SHAPE;   // grid: 4 workgroups per row
+  if (rows < 1 || rows > ((int64_t)1 << 28)) return MLA_ERR_BAD_SHAPE;
   mla::MergeArgs m{};
   m.part_out = (const uint16_t*)part_out;
   m.part_lse = part_lse;
@@ -210,6 +224,7 @@ mla_status mla_merge(const void* part_out, const float* part_lse, int32_t num_sp
   m.lse = lse;
   m.rows = rows;
   m.num_splits = num_splits;
+  if (mla::merge_work_items(m) > mla::kMaxWorkItems) return MLA_ERR_UNSUPPORTED;
   return hip_status(mla::launch_merge(m, (hipStream_t)stream));
 }
 

@@ -69,6 +69,12 @@ struct AppendArgs {
 // launch error.
 hipError_t launch_split(const SplitArgs& a, bool fp8, bool final_out, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+// Work-items (workgroups x threads) the split and merge launches would have:
+// a dispatch packet holds the grid size in 32 bits, so the host rejects a
+// launch above kMaxWorkItems before making it.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+int64_t split_work_items(const SplitArgs& a, bool fp8);
+int64_t merge_work_items(const MergeArgs& a);
 hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_dynamic_scale(const uint16_t* x, int64_t count, float* scale, hipStream_t stream);
 

@@ -160,6 +160,13 @@ hipError_t launch_shape(const MergeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+int64_t merge_work_items(const MergeArgs& a) {
+  // the grids of launch_shape for the shapes launch_merge picks
+  if (a.num_splits <= 8) return (a.rows + 1) / 2 * kMergeThreads;   // two rows per workgroup
+  if (a.num_splits <= 32) return a.rows * kMergeThreads;            // one row per workgroup
+  return a.rows * 4 * kMergeThreads;                                // four quarters per row
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.num_splits <= 8) return launch_shape<1, 512>(a, stream);
   if (a.num_splits <= 32) return launch_shape<2, 512>(a, stream);

@@ -1441,6 +1441,15 @@ hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) 
 
 }  // namespace
 
+int64_t split_work_items(const SplitArgs& a, bool fp8) {
+  // the grids of launch_dtype / launch_layout
+  const int64_t rows = (int64_t)a.num_q * a.heads;
+  const int64_t units = (int64_t)a.num_splits * a.batch;
+  if (fp8 && rows > 32) return units * ((rows + 63) / 64) * kF8Threads;
+  const int64_t rpad = rows <= 16 ? 16 : 48;
+  return units * ((rows + rpad - 1) / rpad) * kThreads;
+}
+
 hipError_t launch_split(const SplitArgs& a, bool fp8, bool final_out, hipStream_t stream) {
   return fp8 ? launch_dtype<true>(a, final_out, stream) : launch_dtype<false>(a, final_out, stream);
 }

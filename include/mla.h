@@ -61,6 +61,12 @@
  * - Host-side validation runs before any HIP call; a failing call returns a
  *   status and launches nothing.  After a launch, a HIP error maps to
  *   MLA_ERR_HIP (the code is kept by mla_last_hip_error()).
+ * - A dispatch holds its grid size in 32 bits: a call whose split or merge
+ *   launch would exceed 2^32 - 1 work-items returns MLA_ERR_UNSUPPORTED (for
+ *   example S = 256 with 65,535 sequences of 1,024 query rows; the split
+ *   launch has 256 threads per workgroup and query-row block, 512 for FP8
+ *   with more than 32 rows, the merge 128, 256 or 1,024 threads per row for
+ *   S <= 8, <= 32 or more).
  * - Caller contract, not checked on the device: num_q_tokens <= seq_lens[b]
  *   <= 16 * max_blocks_per_seq and 0 <= page_table[b][p] < num_blocks for the
  *   pages read.  kv_cache and page_table are only read.
@@ -153,7 +159,8 @@ mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
  *     out[r][c] = bf16_rne( sum_s exp(part_lse[s][r] - lse[r]) * part_out[s][r][c] )
  * part_out bf16 [num_splits][rows][512], part_lse fp32 [num_splits][rows],
  * out bf16 [rows][512], lse fp32 [rows].  All partials -inf: out 0, lse -inf.
- * 1 <= num_splits <= 4096, 1 <= rows <= 2^28; otherwise MLA_ERR_BAD_SHAPE.  A
+ * 1 <= num_splits <= 4096, 1 <= rows <= 2^28; otherwise MLA_ERR_BAD_SHAPE
+ * (and MLA_ERR_UNSUPPORTED above 2^32 - 1 work-items, see above).  A
  * partial of weight zero (part_lse = -inf) is never used, whatever part_out
  * holds for it. */
 mla_status mla_merge(const void* part_out, const float* part_lse, int32_t num_splits,

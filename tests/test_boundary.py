@@ -14,7 +14,7 @@ from decode_attention_03_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla.h")
 
-OK, NULL, SHAPE, DTYPE, SCALE, UNSUP, WS, HIP = range(8)
+OK, NULL, SHAPE, DTYPE, SCALE, UNSUPPORTED, WS, HIP = range(8)
 
 
 def _declared():
@@ -129,7 +129,7 @@ def test_validation_errors(lib, entry):
         d = dict(num_q_tokens=q1)
         d.update(bad)
         assert _verify(lib, params(**d), entry=entry) == SHAPE, bad
-    assert _verify(lib, params(num_q_tokens=q1, num_heads=129), entry=entry) == UNSUP
+    assert _verify(lib, params(num_q_tokens=q1, num_heads=129), entry=entry) == UNSUPPORTED
     assert _verify(lib, params(num_q_tokens=q1, kv_dtype=2), entry=entry) == DTYPE
     assert _verify(lib, params(num_q_tokens=q1), ss=float("nan"), entry=entry) == SCALE
     assert _verify(lib, params(num_q_tokens=q1), ss=float("inf"), entry=entry) == SCALE
@@ -139,6 +139,26 @@ def test_validation_errors(lib, entry):
     # workspace missing or too small when more than one split is used
     assert _verify(lib, params(num_q_tokens=q1, num_splits=4), entry=entry) == WS
     assert _verify(lib, params(num_q_tokens=q1, num_splits=4), ws=FAKE, wsb=100, entry=entry) == WS
+
+
+def test_grid_size_limit(lib):
+    # split launch: 256 splits x 65,535 sequences x 16 FP8 row blocks x 512
+    # threads > 2^32 - 1 work-items; rejected before any pointer is touched
+    big = params(batch=65535, num_q_tokens=8, num_heads=128, num_splits=256)
+    assert _verify(lib, big) == UNSUPPORTED
+    assert lib.mla_split(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 0.07, 0.03, FAKE, FAKE,
+                         None) == UNSUPPORTED
+    # bf16, 48-row blocks of 256 threads: 22 blocks x 256 x 65,535 x 256 > 2^32 - 1
+    assert _verify(lib, params(batch=65535, num_q_tokens=8, num_heads=128, num_splits=256,
+                               kv_dtype=0)) == UNSUPPORTED
+    # the split launch fits (33 x 65,535 x 2 row blocks x 512 = 2.2e9) but
+    # the merge of 8.4 M rows at 1,024 threads per row (S > 32) does not
+    fits_split = params(batch=65535, num_q_tokens=8, num_heads=16, num_splits=33)
+    assert _verify(lib, fits_split) == UNSUPPORTED
+    # a large call that fits both launches goes on to the workspace check
+    assert _verify(lib, params(batch=65535, num_q_tokens=3, num_heads=12, num_splits=2)) == WS
+    # mla_merge: 2^22 rows x 1,024 threads (S > 32) = 2^32 > 2^32 - 1
+    assert lib.mla_merge(FAKE, FAKE, 64, 1 << 22, FAKE, FAKE, None) == UNSUPPORTED
 
 
 def test_decode_rejects_multi_token(lib):
