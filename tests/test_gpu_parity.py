@@ -316,6 +316,46 @@ def test_merge_matches_oracle(gpu_lib, S):
     compare(out[fin], lse[fin], ro[fin], rl[fin], "merge")
 
 
+@pytest.mark.parametrize("dt,nq,S", [("fp8", 3, 5), ("bf16", 1, 1)])
+def test_graph_replay_matches_eager(gpu_lib, dt, nq, S):
+    """bench.py times the path as a replayed HIP graph: every replay, with
+    eager work and synchronisations between replays, reproduces the eager
+    result bit for bit (split + merge with S = 5; one direct launch with S = 1)."""
+    _say(f"graph replay {dt} Q={nq} S={S}")
+    lens = [300, 1500, 40]
+    inp = make_inputs(lens, nq, 12, dt, seed=21 + nq, device="cuda")
+    hint = max(lens)
+    ws = torch.empty(max(256, gpu_lib.workspace_size(inp.q, inp.kv, inp.page_table, S, hint)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((len(lens), nq, 12, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((len(lens), nq, 12), dtype=torch.float32, device="cuda")
+
+    def call():
+        gpu_lib.verify(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
+                       inp.kv_scale, num_splits=S, max_seq_len_hint=hint, out=out, lse=lse,
+                       workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    out_e, lse_e = out.clone(), lse.clone()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        call()
+    torch.cuda.current_stream().wait_stream(st)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        call()
+    for i in range(4):
+        out.zero_()
+        lse.zero_()
+        ws.fill_(0xFF)   # stale workspace contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_e) and torch.equal(lse, lse_e), f"replay {i}"
+
+
 def test_deterministic_and_inputs_untouched(gpu_lib):
     inp = make_inputs([300, 1234, 17], 3, 12, "fp8", seed=9, device="cuda")
     kv0, pt0, q0 = inp.kv.clone(), inp.page_table.clone(), inp.q.clone()
