@@ -356,6 +356,44 @@ def test_graph_replay_matches_eager(gpu_lib, dt, nq, S):
         assert torch.equal(out, out_e) and torch.equal(lse, lse_e), f"replay {i}"
 
 
+def test_split_then_merge_equals_verify(gpu_lib):
+    """mla_split followed by mla_merge on the same S is the verify call's own
+    two launches: bitwise the same output and lse."""
+    lens = [700, 2100, 65]
+    inp = make_inputs(lens, 3, 12, "fp8", seed=23, device="cuda")
+    S = 7
+    out_v, lse_v = run_verify(gpu_lib, inp, num_splits=S)
+    po, pl = gpu_lib.split(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
+                           inp.kv_scale, num_splits=S)
+    out_m, lse_m = gpu_lib.merge(po, pl)
+    torch.cuda.synchronize()
+    assert torch.equal(out_m, out_v) and torch.equal(lse_m, lse_v)
+
+
+def test_concurrent_streams(gpu_lib):
+    """Calls on two streams at once, with their own outputs and workspaces,
+    give what they give one after the other (the library keeps no state
+    between calls)."""
+    a = make_inputs([900, 3000], 3, 12, "fp8", seed=24, device="cuda")
+    b = make_inputs([1200, 64, 5000], 1, 12, "bf16", seed=25, device="cuda")
+    ref_a = run_verify(gpu_lib, a, num_splits=6)
+    ref_b = run_verify(gpu_lib, b, num_splits=3)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    res = {}
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            res["a"] = gpu_lib.verify(a.q, a.kv, a.page_table, a.seq_lens, a.softmax_scale,
+                                      a.kv_scale, num_splits=6)
+        with torch.cuda.stream(s2):
+            res["b"] = gpu_lib.verify(b.q, b.kv, b.page_table, b.seq_lens, b.softmax_scale,
+                                      b.kv_scale, num_splits=3)
+        torch.cuda.synchronize()
+        for key, ref in (("a", ref_a), ("b", ref_b)):
+            assert torch.equal(res[key][0], ref[0]) and torch.equal(res[key][1], ref[1]), (key, rep)
+
+
 def test_deterministic_and_inputs_untouched(gpu_lib):
     inp = make_inputs([300, 1234, 17], 3, 12, "fp8", seed=9, device="cuda")
     kv0, pt0, q0 = inp.kv.clone(), inp.page_table.clone(), inp.q.clone()
