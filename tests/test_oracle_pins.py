@@ -414,6 +414,19 @@ def _decode_kv_no_scale(raw, kv_dtype, kv_scale=1.0):
     return _ORIG_DECODE(raw, kv_dtype, 1.0)
 
 
+def _decode_kv_fp8_bias8(raw, kv_dtype, kv_scale=1.0):     # E4M3 exponent bias 8, not 7
+    x = _ORIG_DECODE(raw, kv_dtype, kv_scale)
+    return x * 0.5 if kv_dtype == "fp8" else x
+
+
+def _partials_inclusive_end(q_bits, kv_raw, page_table, seq_lens, softmax_scale, ranges,
+                            kv_dtype="bf16", kv_scale=1.0, batch_indices=None):
+    # each split also takes the first position of the next: [lo, hi]
+    wide = [[(lo, hi + 1) for lo, hi in r] for r in ranges]
+    return _ORIG_PARTIALS(q_bits, kv_raw, page_table, seq_lens, softmax_scale, wide, kv_dtype,
+                          kv_scale, batch_indices)
+
+
 def _gather_slot_swap(kv_raw, page_table_row, seq_len, kv_dtype, kv_scale=1.0):
     n_pages = -(-int(seq_len) // 16)
     if n_pages == 0:
@@ -428,13 +441,15 @@ _ORIG_ATTEND = om.attend
 _ORIG_MERGE = om.merge
 _ORIG_DECODE = om.decode_kv
 _ORIG_GATHER = om.gather_sequence
+_ORIG_PARTIALS = om.mla_partials
 
 MUTANTS = [
     ("attend", _attend_v_tail), ("attend", _attend_no_scale), ("attend", _attend_lse_log2),
     ("attend", _attend_no_max_sub), ("attend", _attend_transposed),
     ("_visible", _visible_off_by_one), ("_visible", _visible_reversed),
     ("merge", _merge_wrong_sign), ("decode_kv", _decode_kv_no_scale),
-    ("gather_sequence", _gather_slot_swap),
+    ("decode_kv", _decode_kv_fp8_bias8), ("gather_sequence", _gather_slot_swap),
+    ("mla_partials", _partials_inclusive_end),
 ]
 
 
@@ -442,9 +457,8 @@ MUTANTS = [
 def test_planted_mistakes(monkeypatch, name, fn):
     """Each planted slip in a copy of the oracle is caught by at least one pin."""
     monkeypatch.setattr(om, name, fn)
-    if name in ("merge", "attend", "gather_sequence"):
-        monkeypatch.setattr(oracle, {"attend": "attend", "merge": "merge",
-                                     "gather_sequence": "gather_sequence"}[name], fn)
+    if name in ("merge", "attend", "gather_sequence", "mla_partials"):
+        monkeypatch.setattr(oracle, name, fn)
     caught = 0
     for pin in ALL_PINS:
         try:
