@@ -685,6 +685,11 @@ __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   // formats 0/0 = FP8 E4M3 for both operands; E8M0 scales 127 = 1.0
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// The same with E8M0 scale code e (2^(e - 127)) on operand B, one code per
+// lane: for B = P^T, lane l's code scales positions 32(l / 32) .. +31 of row l % 32.
+__device__ __forceinline__ f32x16 mfma_f8s(i32x8 a, i32x8 b, f32x16 c, int e) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, e);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -700,10 +705,11 @@ __device__ __forceinline__ void split4_fp8(float v0, float v1, float v2, float v
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(v2 - b23[0], v3 - b23[1], lo, true);
 }
 
-// Byte offset, from a lane's value base, of the 8 positions 8e..8e+7 (e < 4)
+// Byte offset, from a lane's value base, of the 8 positions
+// 32(e/2) + 8(e%2) .. +7 (e < 4, relative to the lane half's first position)
 // of column tile ct of the FP8 PV step (see the PV comment below).
 constexpr int pv_voff(int ct, int e) {
-  return (e >> 1) * KvGeom<true>::kPageB + 8 * (e & 1) * KvGeom<true>::kRowB +
+  return (e >> 1) * 2 * KvGeom<true>::kPageB + 8 * (e & 1) * KvGeom<true>::kRowB +
          16 * (4 * (ct >> 1) + 2 * ((ct ^ e) & 1));
 }
 
@@ -729,9 +735,9 @@ __device__ __forceinline__ i32x8 read_k_f8(uint32_t a0, uint32_t a1) {
 }
 
 // Value offsets of column tiles 0 and 1 (read_v128_f8 checks tiles 2 and 3).
-static_assert(pv_voff(0, 0) == 0 && pv_voff(0, 1) == 4640 && pv_voff(0, 2) == 9216 &&
-              pv_voff(0, 3) == 13856 && pv_voff(1, 0) == 32 && pv_voff(1, 1) == 4608 &&
-              pv_voff(1, 2) == 9248 && pv_voff(1, 3) == 13824, "offsets in read_v128_f8");
+static_assert(pv_voff(0, 0) == 0 && pv_voff(0, 1) == 4640 && pv_voff(0, 2) == 18432 &&
+              pv_voff(0, 3) == 23072 && pv_voff(1, 0) == 32 && pv_voff(1, 1) == 4608 &&
+              pv_voff(1, 2) == 18464 && pv_voff(1, 3) == 23040, "offsets in read_v128_f8");
 
 // Key operands of two consecutive k-steps (offsets OFF and OFF + 64).
 template <int OFF>
@@ -752,76 +758,77 @@ __device__ __forceinline__ void read_k2_f8(uint32_t a0, uint32_t a1, i32x8& k0, 
 constexpr int kF8Waves = 8;
 constexpr int kF8Threads = kF8Waves * 64;
 
-// LDS reads of the start of an MFMA phase, one round trip: the group's four
-// tile maxima and four row sums of row r32 (red_max / red_sum rows are 128
-// bytes apart) and its two probability terms (as read_p32_f8).
-__device__ __forceinline__ void read_phase_f8(uint32_t maddr, uint32_t saddr, uint32_t paddr,
-                                              float (&rm)[4], float (&rs)[4], i32x8 (&pf)[2]) {
-  u32x4 p0, p1, p2, p3;
+// LDS reads of the start of an MFMA phase, one round trip: the block data of
+// row r32 ({f0, f1, sum0, sum1}) and the lane's two probability terms, 2560
+// bytes apart, each 16 bytes of position block 0 and 16 of block 1 (lane half
+// h: positions 16h + 0..15 and 32 + 16h + 0..15).
+__device__ __forceinline__ void read_phase_f8(uint32_t baddr, uint32_t paddr, f32x4& bk, i32x8 (&pf)[2]) {
+  u32x4 b, p0, p1, p2, p3;
   asm volatile(
-      "ds_read_b32 %0, %12\n\t"
-      "ds_read_b32 %1, %12 offset:128\n\t"
-      "ds_read_b32 %2, %12 offset:256\n\t"
-      "ds_read_b32 %3, %12 offset:384\n\t"
-      "ds_read_b32 %4, %13\n\t"
-      "ds_read_b32 %5, %13 offset:128\n\t"
-      "ds_read_b32 %6, %13 offset:256\n\t"
-      "ds_read_b32 %7, %13 offset:384\n\t"
-      "ds_read_b128 %8, %14\n\t"
-      "ds_read_b128 %9, %14 offset:16\n\t"
-      "ds_read_b128 %10, %14 offset:2560\n\t"
-      "ds_read_b128 %11, %14 offset:2576\n\t"
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %6\n\t"
+      "ds_read_b128 %2, %6 offset:32\n\t"
+      "ds_read_b128 %3, %6 offset:2560\n\t"
+      "ds_read_b128 %4, %6 offset:2592\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(rm[0]), "=&v"(rm[1]), "=&v"(rm[2]), "=&v"(rm[3]), "=&v"(rs[0]), "=&v"(rs[1]),
-        "=&v"(rs[2]), "=&v"(rs[3]), "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
-      : "v"(maddr), "v"(saddr), "v"(paddr));
+      : "=&v"(b), "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
+      : "v"(baddr), "v"(paddr));
+  bk = __builtin_bit_cast(f32x4, b);
   pf[0] = __builtin_bit_cast(i32x8, u32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]});
   pf[1] = __builtin_bit_cast(i32x8, u32x8{p2[0], p2[1], p2[2], p2[3], p3[0], p3[1], p3[2], p3[3]});
 }
 
+// LDS stores of the softmax phase, issued from inline assembly for the same
+// reason: as plain stores the compiler waits for every in-flight copy
+// (vmcnt(0)) before them, and the softmax phase is where group 1 issues the
+// next tile's copies.  The stores have no outputs; the workgroup barrier
+// that ends the phase waits for them (lgkmcnt(0)).
+// Two probability terms of one lane: 4-byte runs at +0, +8, +16, +24 of the
+// lane's row offset, the second term 2560 bytes further.
+__device__ __forceinline__ void store_p_f8(uint32_t addr, const int (&hi)[4], const int (&lo)[4]) {
+  asm volatile(
+      "ds_write2_b32 %0, %2, %3 offset1:2\n\t"
+      "ds_write2_b32 %0, %4, %5 offset0:4 offset1:6\n\t"
+      "ds_write2_b32 %1, %6, %7 offset1:2\n\t"
+      "ds_write2_b32 %1, %8, %9 offset0:4 offset1:6"
+      :
+      : "v"(addr), "v"(addr + 2560u), "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(lo[0]),
+        "v"(lo[1]), "v"(lo[2]), "v"(lo[3]));
+}
+// Block data of one (row, block): f at +0, the weight sum at +8 bytes.
+__device__ __forceinline__ void store_blk_f8(uint32_t addr, float f, float ws) {
+  asm volatile("ds_write2_b32 %0, %1, %2 offset1:2" : : "v"(addr), "v"(f), "v"(ws));
+}
+
 // Value operand of one PV step: column tiles 0..3 (128 columns) x positions
-// 32h + 0..31, sixteen transposed reads at the offsets pv_voff(ct, e).
-static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 9280 &&
-              pv_voff(2, 3) == 13920 && pv_voff(3, 0) == 96 && pv_voff(3, 1) == 4672 &&
-              pv_voff(3, 2) == 9312 && pv_voff(3, 3) == 13888, "offsets in read_v128_f8");
+// 16h + 0..15 and 32 + 16h + 0..15, sixteen transposed reads at the offsets
+// pv_voff(ct, e).
+static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 18496 &&
+              pv_voff(2, 3) == 23136 && pv_voff(3, 0) == 96 && pv_voff(3, 1) == 4672 &&
+              pv_voff(3, 2) == 18528 && pv_voff(3, 3) == 23104, "offsets in read_v128_f8");
 __device__ __forceinline__ void read_v128_f8(uint32_t vaddr, u32x2 (&v)[16]) {
   asm volatile(
       "ds_read_b64_tr_b8 %0, %16\n\t"
       "ds_read_b64_tr_b8 %1, %16 offset:4640\n\t"
-      "ds_read_b64_tr_b8 %2, %16 offset:9216\n\t"
-      "ds_read_b64_tr_b8 %3, %16 offset:13856\n\t"
+      "ds_read_b64_tr_b8 %2, %16 offset:18432\n\t"
+      "ds_read_b64_tr_b8 %3, %16 offset:23072\n\t"
       "ds_read_b64_tr_b8 %4, %16 offset:32\n\t"
       "ds_read_b64_tr_b8 %5, %16 offset:4608\n\t"
-      "ds_read_b64_tr_b8 %6, %16 offset:9248\n\t"
-      "ds_read_b64_tr_b8 %7, %16 offset:13824\n\t"
+      "ds_read_b64_tr_b8 %6, %16 offset:18464\n\t"
+      "ds_read_b64_tr_b8 %7, %16 offset:23040\n\t"
       "ds_read_b64_tr_b8 %8, %16 offset:64\n\t"
       "ds_read_b64_tr_b8 %9, %16 offset:4704\n\t"
-      "ds_read_b64_tr_b8 %10, %16 offset:9280\n\t"
-      "ds_read_b64_tr_b8 %11, %16 offset:13920\n\t"
+      "ds_read_b64_tr_b8 %10, %16 offset:18496\n\t"
+      "ds_read_b64_tr_b8 %11, %16 offset:23136\n\t"
       "ds_read_b64_tr_b8 %12, %16 offset:96\n\t"
       "ds_read_b64_tr_b8 %13, %16 offset:4672\n\t"
-      "ds_read_b64_tr_b8 %14, %16 offset:9312\n\t"
-      "ds_read_b64_tr_b8 %15, %16 offset:13888\n\t"
+      "ds_read_b64_tr_b8 %14, %16 offset:18528\n\t"
+      "ds_read_b64_tr_b8 %15, %16 offset:23104\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
         "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
         "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
       : "v"(vaddr));
-}
-
-// The two probability terms (32 bytes each) of one lane's row, 2560 bytes apart.
-__device__ __forceinline__ void read_p32_f8(uint32_t paddr, i32x8 (&pf)[2]) {
-  u32x4 a0, a1, b0, b1;
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:16\n\t"
-      "ds_read_b128 %2, %4 offset:2560\n\t"
-      "ds_read_b128 %3, %4 offset:2576\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
-      : "v"(paddr));
-  pf[0] = __builtin_bit_cast(i32x8, u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-  pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
 }
 
 // A lane's query fragments from the block staged in LDS (see the prologue of
@@ -889,12 +896,12 @@ __device__ __forceinline__ void read_q_f8(const uint32_t (&a)[4], u32x4 (&v)[5][
 // Eight waves in two groups of four; group g owns query rows 32g..32g+31 and
 // waves 4g..4g+3, and SIMD k runs wave k of group 0 and wave k of group 1.
 // Within a group, wave v = w & 3:
-//   QK:  position half sp = v & 1 of the 64-position tile and dimension half
-//        dh = v >> 1 (k-steps 0..4 or 5..8 of 64 dims): 80 registers of query
-//        fragments.  Partners v and v ^ 2 add their partial scores through
-//        LDS; the dh = 1 wave reads its key rows rotated by 16 positions, so
-//        both keep accumulator elements 0..7 (positions 16dh + 0..15 of the
-//        half) and send elements 8..15.
+//   QK:  position half sp = v & 1 of the 64-position tile (a 32-position
+//        block) and dimension half dh = v >> 1 (k-steps 0..4 or 5..8 of 64
+//        dims): 80 registers of query fragments.  Partners v and v ^ 2 add
+//        their partial scores through LDS by rows: wave dh takes rows
+//        16dh..16dh+15 of its block and hands the partner the other 16, so
+//        that all 32 scores of a (row, block) end up in one wave.
 //   PV:  output columns 128v..128v+127 for the group's 32 rows.
 // The groups run one phase apart (each phase ends with a workgroup barrier):
 //   phase E(i): group 0: PV(i-1), QK(i)   | group 1: softmax(i-1)
@@ -903,10 +910,28 @@ __device__ __forceinline__ void read_q_f8(const uint32_t (&a)[4], u32x4 (&v)[5][
 // arithmetic.  QK(i) also reads the tile's value fragments into registers,
 // so a tile is only read in E(i) and O(i): buffer (i + 2) % 3 can be refilled
 // at the start of E(i), two tiles ahead.
-// Probabilities use a per-row reference maximum that moves only when a tile
-// maximum exceeds it by more than 2^kSlack; the check runs at the start of
-// the phase after each softmax, on data every wave reads, so the rare
-// recomputation (and its barriers) is taken by all waves together.
+//
+// Probabilities enter the FP8 PV product as two E4M3 terms per value, scaled
+// per (row, 32-position block).  E4M3 spans only about 18 binades, while a
+// long history can hold most of its probability mass far below its maximum
+// (tens of thousands of positions ten nats down carry more mass than the top
+// one), so one scale per row would round that mass away, and FP32
+// accumulation cannot bring back what the operand lost ("Inside Kimi K3
+// optimization", technical note "KDA precision & on-chip memory").  Each
+// block is therefore stored against its own maximum bm (log2 units): with
+// f = floor(bm), x = 2^(s - f + 7) lies in [0, 256) with the block's largest
+// value in [128, 256), x ~ hi + lo (hi = E4M3(x), lo = E4M3(x - hi)), and the
+// MFMA's E8M0 block scale for operand B, 2^(f - 7 - m), restores the
+// magnitude against the row's integer reference maximum m.  Per value
+// |x - (hi + lo)| <= max(2^-8 x, 2^-10), so each block's weights are off by
+// at most 2^-8 of its mass plus 2^-12 of its largest value: relative error
+// <= 2^-8 + 2^-12 on the whole weight vector of a row, however wide the
+// spread of the scores, hence |dout| <= (2^-8 + 2^-12) max|v|.  The row sum
+// (and so lse) adds the fp32 x: a sum of the stored terms would carry their
+// 2^-8 error into lse, up to 4e-3 in a row dominated by one position.  The
+// reference m only sets the exponent range of the fp32 accumulators: it
+// moves (by an exact power of two applied to O and l) when a tile maximum
+// passes it by more than 2^kSlack, and nothing is ever recomputed.
 template <bool FINAL>
 __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -916,18 +941,20 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   constexpr int kWaveLoads = G::kPageB / 1024;            // 9 wave-wide 1 KiB copies per page
   constexpr int kPRB = kTilePos + 16;                     // bytes per FP8 probability row (+skew)
   constexpr int kPTerm = 32 * kPRB;                       // 2560: second probability term
-  constexpr float kSlack = 4.f;                           // p * 2^kPShift <= 256
-  constexpr float kPShift = 4.f;
-  static_assert(kPTerm == 2560, "read_p32_f8 assumes 2560 bytes between the terms");
+  // the reference maximum moves when a tile maximum passes it by more than
+  // this (log2 units): stored weights stay below 2^(kSlack + 1), far from
+  // fp32 overflow, and E8M0 block scales below 2^(kSlack - 7)
+  constexpr float kSlack = 16.f;
+  // floor of the maximum of a block with no visible position (its weights are 0)
+  constexpr float kEmptyBlock = -1.0e30f;
+  static_assert(kPTerm == 2560, "read_phase_f8 assumes 2560 bytes between the terms");
 
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][2 * kPTerm];   // [group][term][row][position]
-  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][2][64];    // partial scores for the partner
-  // tile maxima and row sums of each wave's rows, in one array so that the
-  // two addresses of a row differ by a constant
-  __shared__ float red[2][kF8Waves][32];
-  float (&red_max)[kF8Waves][32] = red[0];
-  float (&red_sum)[kF8Waves][32] = red[1];
+  // partial scores for the partner: 16 per lane of the 32 lanes whose rows it takes
+  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][4][32];
+  // per group and row: {f of block 0, f of block 1, fp32 weight sum of block 0, of block 1}
+  __shared__ __attribute__((aligned(16))) f32x4 blk[2][32];
   __shared__ float qmax[kF8Waves][32];
 
   const int tid = threadIdx.x;
@@ -935,7 +962,6 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int h = lane >> 5;
-  const int g16 = lane >> 4;
   const int grp = w >> 2;
   const int v4 = w & 3;
   const int sp = v4 & 1;
@@ -1100,24 +1126,20 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // scale of this lane's scores (row `myrow`) into the log2 domain
   const float cs = a.score_scale_log2 * q_unscale;
 
-  // Reference maxima of rows r32 of group 0 and group 1 (every wave tracks
-  // both, from the same LDS data), the row sum of this wave's row, and the
-  // output of this wave's 128 columns x the group's 32 rows.
-  float mref0 = kNegInf, mref1 = kNegInf;
+  // Integer reference maximum of row r32 of this wave's group (log2 units),
+  // the row sum and the output of this wave's 128 columns x the group's 32
+  // rows, all relative to 2^mref.
+  float mref = kNegInf;
   float l_run = 0.f;
   f32x16 o[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) o[c] = f32x16{};
   i32x8 vfr[4];     // value fragments of the group's next PV
-  float x[8];       // scores of this wave's last softmax (kept for a recomputation)
-#pragma unroll
-  for (int k = 0; k < 8; ++k) x[k] = kNegInf;
+  // this wave's partial scores of its block for the lanes whose rows it
+  // takes (the other lanes' partials went to the partner), kept from QK to
+  // the softmax of the next phase
+  float x[16];
 
-  const int prow = r32 & 15;
-  const int kpage = 2 * sp + ((r32 >> 4) ^ dh);
-  const int sl = lane & 15;
-  const int vbase = 2 * h * G::kPageB + (sl >> 1) * G::kRowB + 16 * (8 * v4 + ((g16 ^ (sl >> 3)) & 1)) + 8 * (sl & 1);
-  const int pbase = r32 * kPRB + 32 * sp + 16 * dh + 4 * h;
   uint8_t* const pg_lds = p_lds[grp];
 
   // An opaque copy of the lane index, taken where a lane-dependent address or
@@ -1137,25 +1159,46 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     asm volatile("" : "+s"(hd));
     return L - a.num_q + (64 * wc.z + 32 * grp + (lane_now() & 31)) / hd + 1;
   };
+  // Lane-dependent LDS offsets, likewise derived where they are used.
+  // Value operand base (see qk below).
+  auto vbase_now = [&]() -> int {
+    const int ln = lane_now();
+    const int s16 = ln & 15;
+    return (ln >> 5) * G::kPageB + (s16 >> 1) * G::kRowB +
+           16 * (8 * v4 + (((ln >> 4) ^ (s16 >> 3)) & 1)) + 8 * (s16 & 1);
+  };
+  // probability bytes of lane (r32, h): row r32, block positions 8q + 4h + 0..3
+  auto pbase_now = [&]() -> int {
+    const int ln = lane_now();
+    return (ln & 31) * kPRB + 32 * sp + 4 * (ln >> 5);
+  };
 
   // ---- a4: partial S^T over this wave's k-steps, then the value fragments.
   // Key addresses of tile T for this wave (lane's row, chunk pair 2h, 2h + 1).
   auto kaddr = [&](int T, uint32_t& kb0, uint32_t& kb1) {
     const uint8_t* tile = kv_lds + (T % kNBuf) * kTileB;
-    kb0 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h, 0) + 64 * ks0);
-    kb1 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * h + 1, 0) + 64 * ks0);
+    const int ln = lane_now();
+    const int prow = ln & 15;
+    const int kpage = 2 * sp + ((ln >> 4) & 1);
+    const int hh = ln >> 5;
+    kb0 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * hh, 0) + 64 * ks0);
+    kb1 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * hh + 1, 0) + 64 * ks0);
   };
   // The value operand for the PV of this tile is read after the last key
   // operands, while the last score MFMAs drain (the tile is not read after
-  // this phase).  Column tile ct, positions 32h + 8e .. +7: source lane sl of
-  // a 16-lane group reads position 32h + 8e + sl/2, i.e. page 2h + e/2, row
-  // 8(e%2) + sl/2, byte half sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by
-  // (row/4)%4 = sl/8 + 2(e%2); vbase is the lane part of that address and
-  // pv_voff(ct, e) the rest.
+  // this phase).  The PV product's K index runs over the tile's 64 positions
+  // so that each 32-index block of its E8M0 scales (bytes 0..15 of both lane
+  // halves, then bytes 16..31 of both) is one position block of the softmax:
+  // lane half h, byte j holds position 32(j/16) + 16h + j%16.  Column tile
+  // ct, bytes 8e .. 8e+7: source lane sl of a 16-lane group reads position
+  // 32(e/2) + 16h + 8(e%2) + sl/2, i.e. page h + 2(e/2), row 8(e%2) + sl/2,
+  // byte half sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by (row/4)%4 =
+  // sl/8 + 2(e%2); vbase is the lane part of that address and pv_voff(ct, e)
+  // the rest.
   auto qk = [&](int T) {
     uint32_t kb0, kb1;
     kaddr(T, kb0, kb1);
-    const uint32_t vaddr = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, kv_lds + (T % kNBuf) * kTileB + vbase);
+    const uint32_t vaddr = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, kv_lds + (T % kNBuf) * kTileB + vbase_now());
     f32x16 s = f32x16{};
     u32x2 vr[16];
     i32x8 ka, kb;
@@ -1184,49 +1227,36 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       vfr[ct] = __builtin_bit_cast(i32x8, u32x8{vr[4 * ct][0], vr[4 * ct][1], vr[4 * ct + 1][0],
                                                 vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
                                                 vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
-    // elements 8..15 belong to the partner wave; elements 0..7 stay for softmax
+    // Rows 16dh..16dh+15 stay with this wave; the partials of the other 16
+    // rows go to the partner (xbuf slot (r32 % 16) + 16h, 16 floats).
     {
       const int ln = lane_now();
-      xbuf[w][0][ln] = f32x4{s[8], s[9], s[10], s[11]};
-      xbuf[w][1][ln] = f32x4{s[12], s[13], s[14], s[15]};
-    }
+      if (((ln >> 4) & 1) != dh) {
+        const int slot = (ln & 15) | ((ln >> 5) << 4);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = s[k];
-  };
-
-  // probabilities p * 2^kPShift against the reference maximum, as two FP8 terms
-  auto probs = [&](float m) {
-    const float c0 = kPShift - (m == kNegInf ? 0.f : m);
-    float ps = 0.f;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float p4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p4[i] = __builtin_amdgcn_exp2f(x[4 * q + i] + c0);
-        ps += p4[i];
+        for (int c = 0; c < 4; ++c) xbuf[w][c][slot] = f32x4{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]};
       }
-      int hi, lo;
-      split4_fp8(p4[0], p4[1], p4[2], p4[3], hi, lo);
-      *(int*)(pg_lds + pbase + 8 * q) = hi;
-      *(int*)(pg_lds + kPTerm + pbase + 8 * q) = lo;
     }
-    ps = sum32(ps);
-    if (h == 0) red_sum[w][r32] = ps;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = s[k];
   };
 
   // ---- a5: partner's partial scores added, scale to log2 units, mask (edge
-  // tiles only), tile maxima, probabilities.  Element k of x is position
-  // 32sp + 16dh + 8(k/4) + 4h + k%4 of the tile.
+  // tiles only), block maximum, probabilities as two FP8 terms against it.
+  // For a lane whose row this wave takes (rows 16dh..16dh+15), element k of
+  // x is position 8(k/4) + 4h + k%4 of block sp; lanes (r32, 0) and (r32, 1)
+  // together hold the whole block.  The other lanes compute on their own
+  // partials and store nothing.
   auto softmax = [&](int T) {
+    const bool mine = ((lane_now() >> 4) & 1) == dh;
     {
       const int ln = lane_now();
-      const f32x4 u0 = xbuf[w ^ 2][0][ln];
-      const f32x4 u1 = xbuf[w ^ 2][1][ln];
+      const int slot = (ln & 15) | ((ln >> 5) << 4);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[k] += u0[k];
-        x[4 + k] += u1[k];
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 u = xbuf[w ^ 2][c][slot];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[4 * c + k] += u[k];
       }
     }
     const int tpos0 = (p0 + T * kTilePages) * kPage;
@@ -1234,101 +1264,97 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     float mx = kNegInf;
     if (tlim >= kTilePos && tpos0 + kTilePos <= L - a.num_q + 1) {   // every row sees the whole tile
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 16; ++k) {
         x[k] *= cs;
         mx = fmaxf(mx, x[k]);
       }
     } else {
-      // position tq = 32 sp + 16 dh + 4 h + (8 (k / 4) + k % 4) is visible
-      // when it is below both tlim and lim - tpos0
-      const int kvis = min(tlim, lim_now() - tpos0) - (32 * sp + 16 * dh + 4 * (lane_now() >> 5));
+      // position tq = 32 sp + 4 h + (8 (k / 4) + k % 4) is visible when it is
+      // below both tlim and lim - tpos0
+      const int kvis = min(tlim, lim_now() - tpos0) - (32 * sp + 4 * (lane_now() >> 5));
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 16; ++k) {
         x[k] = 8 * (k >> 2) + (k & 3) < kvis ? x[k] * cs : kNegInf;
         mx = fmaxf(mx, x[k]);
       }
     }
-    mx = max32(mx);
-    if (h == 0) red_max[w][r32] = mx;
-    probs(grp ? mref1 : mref0);
-  };
-
-  // Start of the phase after group gx's softmax: move gx's reference maxima
-  // where a tile maximum passed them by more than 2^kSlack, and in that (rare,
-  // workgroup-uniform) case let gx recompute its probabilities.  This is the
-  // other group's side (gx != grp): it only tracks gx's maxima and joins the
-  // two barriers.
-  auto check = [&](int gx) {
-    const float nm = fmaxf(fmaxf(red_max[4 * gx][r32], red_max[4 * gx + 1][r32]),
-                           fmaxf(red_max[4 * gx + 2][r32], red_max[4 * gx + 3][r32]));
-    const float mo = gx ? mref1 : mref0;
-    const bool ov = nm > mo + kSlack;
-    if (__any(ov)) {
-      const float mn = ov ? nm : mo;
-      if (gx) mref1 = mn;
-      else mref0 = mn;
-      lds_barrier();   // every wave has read the maxima (and the first sums)
-      lds_barrier();   // gx has recomputed its probabilities
+    mx = max32(mx);                                   // the block's maximum
+    const float f = mx == kNegInf ? kEmptyBlock : floorf(mx);
+    const float c0 = 7.f - f;
+    float ws = 0.f;
+    int hi[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float p4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p4[i] = __builtin_amdgcn_exp2f(x[4 * q + i] + c0);
+      ws += (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      split4_fp8(p4[0], p4[1], p4[2], p4[3], hi[q], lo[q]);
+    }
+    ws = sum32(ws);
+    if (mine) {
+      const uint32_t pa = (uint32_t)(uintptr_t)LDS_PTR(uint8_t, pg_lds + pbase_now());
+      store_p_f8(pa, hi, lo);
+      if (h == 0)
+        store_blk_f8((uint32_t)(uintptr_t)LDS_PTR(float, (float*)&blk[grp][lane_now() & 31] + sp), f, ws);
     }
   };
 
-  // The same check run by the group that ran that softmax (gx = grp), on the
-  // maxima and sums read with its phase's other LDS data; after a
-  // recomputation the probability terms pf are read again.
-  const uint32_t p_addr = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, pg_lds + r32 * kPRB + 32 * h);
-  auto check_own = [&](const float (&rm)[4], const float (&rs)[4], i32x8 (&pf)[2]) -> float {
-    const float nm = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
-    float sm = (rs[0] + rs[1]) + (rs[2] + rs[3]);
-    const float mo = grp ? mref1 : mref0;
-    const bool ov = nm > mo + kSlack;
-    if (__any(ov)) {
-      const float mn = ov ? nm : mo;
-      const float alpha = ov ? __builtin_amdgcn_exp2f(mo - mn) : 1.f;
+  // Start of an MFMA phase: the reference maximum of the lane's row moves to
+  // the tile maximum when that passes it by more than 2^kSlack (O and l are
+  // rescaled by the exact power of two), then the E8M0 codes of the two
+  // blocks against it, 127 + f - 7 - mref (at least 0: a block more than
+  // 2^120 below the reference weighs at most 2^-119 of it), and the row sum
+  // of the tile under the same codes.  Returns the code of the lane's own
+  // block (the B operand's scale of its PV lane).
+  auto rebase = [&](const f32x4 bk) -> int {
+    const float tm = fmaxf(bk[0], bk[1]);
+    const bool mv = tm > mref + kSlack;
+    const float mn = mv ? tm : mref;
+    if (__any(mv)) {
+      const float alpha = mv ? __builtin_amdgcn_exp2f(mref - mn) : 1.f;   // integer argument
       l_run *= alpha;
       o[0] *= alpha;
       o[1] *= alpha;
       o[2] *= alpha;
       o[3] *= alpha;
-      if (grp) mref1 = mn;
-      else mref0 = mn;
-      lds_barrier();
-      probs(mn);
-      lds_barrier();
-      sm = (red_sum[4 * grp][r32] + red_sum[4 * grp + 1][r32]) +
-           (red_sum[4 * grp + 2][r32] + red_sum[4 * grp + 3][r32]);
-      read_p32_f8(p_addr, pf);
     }
-    return sm;
+    mref = mn;
+    const int e0 = (int)fminf(fmaxf(120.f + bk[0] - mn, 0.f), 254.f);
+    const int e1 = (int)fminf(fmaxf(120.f + bk[1] - mn, 0.f), 254.f);
+    l_run += ldexpf(bk[2], e0 - 127) + ldexpf(bk[3], e1 - 127);
+    return h ? e1 : e0;
   };
 
-  // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127.
-  auto pv = [&](float row_sum, const i32x8 (&pf)[2]) {
-    l_run += row_sum;
+  // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127,
+  // with the block's E8M0 scale on operand B.
+  auto pv = [&](int e, const i32x8 (&pf)[2]) {
     // written out: a rolled loop here makes the compiler rotate the four
     // accumulators through one register window with moves
-    o[0] = mfma_f8(vfr[0], pf[0], o[0]);
-    o[1] = mfma_f8(vfr[1], pf[0], o[1]);
-    o[2] = mfma_f8(vfr[2], pf[0], o[2]);
-    o[3] = mfma_f8(vfr[3], pf[0], o[3]);
-    o[0] = mfma_f8(vfr[0], pf[1], o[0]);
-    o[1] = mfma_f8(vfr[1], pf[1], o[1]);
-    o[2] = mfma_f8(vfr[2], pf[1], o[2]);
-    o[3] = mfma_f8(vfr[3], pf[1], o[3]);
+    o[0] = mfma_f8s(vfr[0], pf[0], o[0], e);
+    o[1] = mfma_f8s(vfr[1], pf[0], o[1], e);
+    o[2] = mfma_f8s(vfr[2], pf[0], o[2], e);
+    o[3] = mfma_f8s(vfr[3], pf[0], o[3], e);
+    o[0] = mfma_f8s(vfr[0], pf[1], o[0], e);
+    o[1] = mfma_f8s(vfr[1], pf[1], o[1], e);
+    o[2] = mfma_f8s(vfr[2], pf[1], o[2], e);
+    o[3] = mfma_f8s(vfr[3], pf[1], o[3], e);
   };
 
-  // Half-steps hs = 0, 1, ...: E(i) = 2i, O(i) = 2i + 1.  Group g's own step
-  // count is hs - g: even -> MFMA role (PV of tile T - 1, QK of tile T,
-  // T = (hs - g) / 2), odd -> softmax of tile T = (hs - g - 1) / 2.  At each
-  // half-step the group that ran its softmax in the previous one (g = hs % 2)
-  // is checked first.
+  // Half-steps hs = 0, 1, ...: E(i) = 2i, O(i) = 2i + 1.  Group 0 runs
+  // MFMA(T) (PV of tile T - 1, QK of tile T) at hs = 2T and softmax(T) at
+  // 2T + 1; group 1 one half-step later, after an idle first one.  Each
+  // group's loop holds one MFMA phase and one softmax phase, so the partial
+  // scores passed from QK to the softmax are dead across iterations.  Both
+  // groups start 2 ntiles + 2 half-steps, each with one workgroup barrier.
   // Tile 0 (group 0's prologue copies) has landed before the loop; tile 1
   // (group 1's) only before E(1).
-  if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
+  // Start of a half-step.  Group 1 copies at every even one (hs = 0 and the
+  // starts of its softmax phases): its vector-memory order is copies(1),
+  // PT(4), copies(2), PT(5), copies(3) ...; before E(T), T >= 1, copies(T)
+  // must have landed while PT(T + 3) and copies(T + 1) may still be in flight.
+  auto begin = [&](int hs) {
     const bool copier = grp == 1 && (hs & 1) == 0;
-    // Group 1's vector-memory order: copies(1), PT(4), copies(2), PT(5),
-    // copies(3) ...  Before E(T), T >= 1, copies(T) must have landed while
-    // PT(T + 3) and copies(T + 1) may still be in flight.
     if (copier && hs >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads + 1));
     lds_barrier();
     if (copier) {
@@ -1343,29 +1369,34 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       if (it & 1) ptB = nxt;
       else ptA = nxt;
     }
+  };
+  // MFMA role: one LDS round trip for the block data and the PV's
+  // probabilities (stale data where unused); the phase's critical path, so
+  // its instructions go first on the SIMD it shares with a softmax-role wave.
+  auto mfma_phase = [&](int T, bool with_qk) {
+    __builtin_amdgcn_s_setprio(2);
+    f32x4 bk;
+    i32x8 pf[2];
+    {
+      const int ln = lane_now();
+      read_phase_f8((uint32_t)(uintptr_t)LDS_PTR(const f32x4, &blk[grp][ln & 31]),
+                    (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, pg_lds + (ln & 31) * kPRB + 16 * (ln >> 5)),
+                    bk, pf);
+    }
+    if (T >= 1) pv(rebase(bk), pf);
+    if (with_qk) qk(T);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
+    begin(hs);
     const int st = hs - grp;
     if (st >= 0 && (st & 1) == 0) {
-      // MFMA role (grp == hs % 2): one LDS round trip for the check and the
-      // PV's probabilities (stale data where unused)
       const int T = st >> 1;
-      // the MFMA role is the phase's critical path: its instructions go first
-      // on the SIMD it shares with a softmax-role wave
-      __builtin_amdgcn_s_setprio(2);
-      float rm[4], rs[4];
-      i32x8 pf[2];
-      read_phase_f8((uint32_t)(uintptr_t)LDS_PTR(const float, &red_max[4 * grp][r32]),
-                    (uint32_t)(uintptr_t)LDS_PTR(const float, &red_sum[4 * grp][r32]), p_addr, rm, rs,
-                    pf);
-      const float row_sum = hs >= 2 ? check_own(rm, rs, pf) : 0.f;
-      if (T >= 1) pv(row_sum, pf);
-      if (T < ntiles) qk(T);
-      __builtin_amdgcn_s_setprio(0);
-    } else {
-      if (hs >= 2) check(hs & 1);
-      if (st >= 1) {
-        const int T = (st - 1) >> 1;
-        if (T < ntiles) softmax(T);
-      }
+      mfma_phase(T, T < ntiles);
+    } else if (st >= 1) {
+      const int T = (st - 1) >> 1;
+      if (T < ntiles) softmax(T);
     }
   }
 
@@ -1374,7 +1405,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();
 
-  // ---- a7: epilogue.  O and l both carry the 2^kPShift factor.  Each wave's
+  // ---- a7: epilogue.  O and l are relative to 2^mref.  Each wave's
   // 32 rows x 128 columns go through LDS (the free KV buffers) so that a store
   // instruction writes four whole 256-byte row segments; stored straight from
   // the accumulators, each instruction would touch 32 rows with 16 bytes each.
@@ -1405,7 +1436,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     }
   }
   if (myrow < R && v4 == 0 && h == 0) {
-    const float lv = (l_run > 0.f) ? ((grp ? mref1 : mref0) - kPShift + log2f(l_run)) * kLn2 : kNegInf;
+    const float lv = (l_run > 0.f) ? (mref + log2f(l_run)) * kLn2 : kNegInf;
     if constexpr (FINAL) a.lse[(int64_t)b * R + myrow] = lv;
     else a.part_lse[((int64_t)split * a.batch + b) * R + myrow] = lv;
   }

@@ -199,6 +199,80 @@ def test_fp8_growing_scores(gpu_lib, alpha):
         compare(out, lse, ro, rl, f"alpha={alpha} S={S}", lse_tol=lse_tol)
 
 
+def _dominant_key_inputs(lens, gap_nat, body_std, tied, key_pos, seed):
+    """FP8 verify inputs whose scores (from the 64 rope dims only) put one key
+    gap_nat nats above a body of near-equal scores (std body_std nats, or
+    exactly tied), with value vectors of mean +0.3.  The body's total
+    probability mass is then comparable to the key's, and far below it per
+    position: the case where a probability format of narrow range loses mass.
+    Head h scales the query, so the rows span 0.5x .. 1.5x the gap."""
+    inp = make_inputs(lens, 3, 12, "fp8", seed=seed, device="cpu")
+    g = torch.Generator().manual_seed(seed)
+    nb = inp.kv.shape[0]
+    lat = torch.randn((nb, 16, 576), generator=g) * 0.5
+    lat[:, :, :512] += 0.3
+    u = torch.ones(64) / 8.0                        # unit vector over the rope dims
+    sc = float(inp.softmax_scale)
+    beta = max(body_std, 0.3) / (sc * 0.5)          # body score std = body_std nats
+    c = gap_nat / (sc * beta)                       # the key's rope part, along u
+    pt = inp.page_table.numpy()
+    for b, L in enumerate(lens):
+        if tied:
+            for p in range(-(-L // 16)):
+                lat[int(pt[b, p]), :, 512:] = 0.02 * u
+        t = key_pos if key_pos >= 0 else L + key_pos
+        lat[int(pt[b, t // 16]), t % 16, 512:] = c * u
+    amax = float(lat.abs().max())
+    kv_scale = float(np.float32(amax / 448.0))
+    inp.kv = (lat / kv_scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    inp.kv_scale = kv_scale
+    q = torch.zeros((len(lens), 3, 12, 576))
+    for hh in range(12):
+        q[:, :, hh, 512:] = beta * (0.5 + hh / 11.0) * u
+    inp.q = q.to(torch.bfloat16)
+    return workloads.MLAInputs(q=inp.q.cuda(), kv=inp.kv.cuda(), page_table=inp.page_table.cuda(),
+                               seq_lens=inp.seq_lens.cuda(), kv_dtype="fp8", kv_scale=kv_scale,
+                               softmax_scale=inp.softmax_scale, meta={})
+
+
+DOMINANT_KEY_CASES = [
+    # (seq_lens, gap in nats, body std in nats, tied body, key position (<0: from the end))
+    ([35500], 10.0, 0.3, False, 5),
+    ([35500], 10.0, 0.3, False, -40),
+    ([35500, 3000], 14.0, 0.0, True, 5),
+    ([35500], 7.0, 1.0, False, 20000),
+]
+
+
+@pytest.mark.parametrize("case", DOMINANT_KEY_CASES,
+                         ids=[f"L{c[0][0]}-gap{c[1]:g}-std{c[2]:g}-{'tied' if c[3] else 'rand'}-key{c[4]}"
+                              for c in DOMINANT_KEY_CASES])
+def test_fp8_dominant_key_over_flat_body(gpu_lib, case):
+    """One key several nats above tens of thousands of near-equal scores:
+    most of the probability mass sits far below the maximum.  Every split
+    count (one split over the whole history, the 8 chunks of the long-context
+    workload, the automatic count) must match the oracle."""
+    lens, gap, std, tied, kp = case
+    _say(f"dominant key {case}")
+    inp = _dominant_key_inputs(lens, gap, std, tied, kp, seed=31 + int(gap))
+    ro, rl, _ = oracle_out(inp)
+    for S in (1, 8, 0):
+        out, lse = run_verify(gpu_lib, inp, num_splits=S)
+        dout, dlse = compare(out, lse, ro, rl, f"{case} S={S}")
+        _say(f"  S={S}: max|dout|/max|ref| = {dout:.3e}, max|dlse| = {dlse:.3e}")
+
+
+def test_fp8_dominant_key_long_sequence_c4_splits(gpu_lib):
+    """The same structure over 65,536 positions at the split count of the
+    B = 64 FP8 verify workload (32)."""
+    _say("dominant key, 65,536 positions, S = 32")
+    inp = _dominant_key_inputs([65536], 12.0, 1.0, False, 40000, seed=65)
+    ro, rl, _ = oracle_out(inp)
+    out, lse = run_verify(gpu_lib, inp, num_splits=32)
+    dout, dlse = compare(out, lse, ro, rl, "65536 S=32")
+    _say(f"  max|dout|/max|ref| = {dout:.3e}, max|dlse| = {dlse:.3e}")
+
+
 def test_c6_dcp8_shaped_sampled(gpu_lib):
     _say("config c6")
     inp = make_config("c6", device="cuda")
