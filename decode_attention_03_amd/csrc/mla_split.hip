@@ -129,6 +129,16 @@ __device__ __forceinline__ float sum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
+// x combined with the value of lane l ^ 16 (a VALU row swap); both lanes of
+// a pair add in the same order
+__device__ __forceinline__ float max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // 8 FP8 E4M3FN codes (two dwords) -> 8 bf16 (exact).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 raw) {
@@ -783,17 +793,14 @@ __device__ __forceinline__ void read_phase_f8(uint32_t baddr, uint32_t paddr, f3
 // (vmcnt(0)) before them, and the softmax phase is where group 1 issues the
 // next tile's copies.  The stores have no outputs; the workgroup barrier
 // that ends the phase waits for them (lgkmcnt(0)).
-// Two probability terms of one lane: 4-byte runs at +0, +8, +16, +24 of the
-// lane's row offset, the second term 2560 bytes further.
-__device__ __forceinline__ void store_p_f8(uint32_t addr, const int (&hi)[4], const int (&lo)[4]) {
+// Two probability terms of one lane: 4-byte runs at +0 and +8 of the lane's
+// offset, the second term 2560 bytes further.
+__device__ __forceinline__ void store_p_f8(uint32_t addr, const int (&hi)[2], const int (&lo)[2]) {
   asm volatile(
       "ds_write2_b32 %0, %2, %3 offset1:2\n\t"
-      "ds_write2_b32 %0, %4, %5 offset0:4 offset1:6\n\t"
-      "ds_write2_b32 %1, %6, %7 offset1:2\n\t"
-      "ds_write2_b32 %1, %8, %9 offset0:4 offset1:6"
+      "ds_write2_b32 %1, %4, %5 offset1:2"
       :
-      : "v"(addr), "v"(addr + 2560u), "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(lo[0]),
-        "v"(lo[1]), "v"(lo[2]), "v"(lo[3]));
+      : "v"(addr), "v"(addr + 2560u), "v"(hi[0]), "v"(hi[1]), "v"(lo[0]), "v"(lo[1]));
 }
 // Block data of one (row, block): f at +0, the weight sum at +8 bytes.
 __device__ __forceinline__ void store_blk_f8(uint32_t addr, float f, float ws) {
@@ -952,7 +959,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][2 * kPTerm];   // [group][term][row][position]
   // partial scores for the partner: 16 per lane of the 32 lanes whose rows it takes
-  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][4][32];
+  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][2][64];
   // per group and row: {f of block 0, f of block 1, fp32 weight sum of block 0, of block 1}
   __shared__ __attribute__((aligned(16))) f32x4 blk[2][32];
   __shared__ float qmax[kF8Waves][32];
@@ -1123,8 +1130,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       q2[ks] = lo8;
     }
   }
-  // scale of this lane's scores (row `myrow`) into the log2 domain
-  const float cs = a.score_scale_log2 * q_unscale;
+  // scale into the log2 domain of the scores this lane handles in the
+  // softmax: row 16dh + l % 16 of the group (q_unscale is per row, held by
+  // lane l for row l % 32)
+  float cs;
+  {
+    const float c = a.score_scale_log2 * q_unscale;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+    cs = __uint_as_float(dh ? r[1] : r[0]);
+  }
 
   // Integer reference maximum of row r32 of this wave's group (log2 units),
   // the row sum and the output of this wave's 128 columns x the group's 32
@@ -1135,10 +1149,9 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 #pragma unroll
   for (int c = 0; c < 4; ++c) o[c] = f32x16{};
   i32x8 vfr[4];     // value fragments of the group's next PV
-  // this wave's partial scores of its block for the lanes whose rows it
-  // takes (the other lanes' partials went to the partner), kept from QK to
-  // the softmax of the next phase
-  float x[16];
+  // this wave's partial scores kept from QK for the softmax of the next
+  // phase: 8 of one row of 16dh..16dh+15 per lane (see qk)
+  float x[8];
 
   uint8_t* const pg_lds = p_lds[grp];
 
@@ -1151,13 +1164,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     asm volatile("" : "+v"(l));
     return l;
   };
-  // Causal limit of the lane's row (visible: position < lim), needed on edge
-  // tiles only and recomputed there (with an opaque divisor, so that the
-  // division's reciprocal is not kept either).
+  // Row (within the group) of the lane's scores in the softmax: 16dh + l % 16.
+  auto srow_now = [&]() -> int { return (lane_now() & 15) + 16 * dh; };
+  // Causal limit of that row (visible: position < lim), needed on edge tiles
+  // only and recomputed there (with an opaque divisor, so that the division's
+  // reciprocal is not kept either).
   auto lim_now = [&]() -> int {
     int hd = H;
     asm volatile("" : "+s"(hd));
-    return L - a.num_q + (64 * wc.z + 32 * grp + (lane_now() & 31)) / hd + 1;
+    return L - a.num_q + (64 * wc.z + 32 * grp + srow_now()) / hd + 1;
   };
   // Lane-dependent LDS offsets, likewise derived where they are used.
   // Value operand base (see qk below).
@@ -1167,10 +1182,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     return (ln >> 5) * G::kPageB + (s16 >> 1) * G::kRowB +
            16 * (8 * v4 + (((ln >> 4) ^ (s16 >> 3)) & 1)) + 8 * (s16 & 1);
   };
-  // probability bytes of lane (r32, h): row r32, block positions 8q + 4h + 0..3
-  auto pbase_now = [&]() -> int {
+  // First position (within the block) of the lane's softmax scores: they
+  // are 16u + 8(k/4) + 4h + k%4, k < 8, with u = 1 for the lanes that hold
+  // elements 8..15 of their row (lanes of rows 16..31, see qk).
+  auto spos_now = [&]() -> int {
     const int ln = lane_now();
-    return (ln & 31) * kPRB + 32 * sp + 4 * (ln >> 5);
+    return 16 * ((ln >> 4) & 1) + 4 * (ln >> 5);
   };
 
   // ---- a4: partial S^T over this wave's k-steps, then the value fragments.
@@ -1227,36 +1244,53 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       vfr[ct] = __builtin_bit_cast(i32x8, u32x8{vr[4 * ct][0], vr[4 * ct][1], vr[4 * ct + 1][0],
                                                 vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
                                                 vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
-    // Rows 16dh..16dh+15 stay with this wave; the partials of the other 16
-    // rows go to the partner (xbuf slot (r32 % 16) + 16h, 16 floats).
+    // Rows 16dh..16dh+15 stay with this wave, the other 16 go to the
+    // partner, 8 scores per lane either way.  Lane l (row l % 32, position
+    // half h) holds elements 0..15 of its row.  One lane swap between lanes
+    // l and l ^ 16 per element pair (k, k + 8) leaves in every lane 8 values
+    // to keep and 8 to send; the partner's lane l keeps the sent ones.  With
+    // dh = 0 the lanes of rows 0..15 keep their elements 0..7 and the lanes
+    // of rows 16..31 elements 8..15 of row (l % 32) - 16; with dh = 1 the
+    // lanes of rows 16..31 keep their elements 8..15 and the lanes of rows
+    // 0..15 elements 0..7 of row (l % 32) + 16.
     {
-      const int ln = lane_now();
-      if (((ln >> 4) & 1) != dh) {
-        const int slot = (ln & 15) | ((ln >> 5) << 4);
+      uint32_t r0[8], r1[8];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xbuf[w][c][slot] = f32x4{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]};
+      for (int k = 0; k < 8; ++k) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[k]), __float_as_uint(s[k + 8]),
+                                                        false, false);
+        r0[k] = r[0];
+        r1[k] = r[1];
+      }
+      const int ln = lane_now();
+      if (dh) {
+        xbuf[w][0][ln] = __builtin_bit_cast(f32x4, u32x4{r0[0], r0[1], r0[2], r0[3]});
+        xbuf[w][1][ln] = __builtin_bit_cast(f32x4, u32x4{r0[4], r0[5], r0[6], r0[7]});
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = __uint_as_float(r1[k]);
+      } else {
+        xbuf[w][0][ln] = __builtin_bit_cast(f32x4, u32x4{r1[0], r1[1], r1[2], r1[3]});
+        xbuf[w][1][ln] = __builtin_bit_cast(f32x4, u32x4{r1[4], r1[5], r1[6], r1[7]});
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = __uint_as_float(r0[k]);
       }
     }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) x[k] = s[k];
   };
 
   // ---- a5: partner's partial scores added, scale to log2 units, mask (edge
   // tiles only), block maximum, probabilities as two FP8 terms against it.
-  // For a lane whose row this wave takes (rows 16dh..16dh+15), element k of
-  // x is position 8(k/4) + 4h + k%4 of block sp; lanes (r32, 0) and (r32, 1)
-  // together hold the whole block.  The other lanes compute on their own
-  // partials and store nothing.
+  // Element k of x is position spos + 8(k/4) + k%4 of block sp of row
+  // 16dh + l % 16; lanes l, l ^ 16, l ^ 32 and l ^ 48 together hold the
+  // row's whole block.
   auto softmax = [&](int T) {
-    const bool mine = ((lane_now() >> 4) & 1) == dh;
     {
       const int ln = lane_now();
-      const int slot = (ln & 15) | ((ln >> 5) << 4);
+      const f32x4 u0 = xbuf[w ^ 2][0][ln];
+      const f32x4 u1 = xbuf[w ^ 2][1][ln];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 u = xbuf[w ^ 2][c][slot];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[4 * c + k] += u[k];
+      for (int k = 0; k < 4; ++k) {
+        x[k] += u0[k];
+        x[4 + k] += u1[k];
       }
     }
     const int tpos0 = (p0 + T * kTilePages) * kPage;
@@ -1264,39 +1298,40 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     float mx = kNegInf;
     if (tlim >= kTilePos && tpos0 + kTilePos <= L - a.num_q + 1) {   // every row sees the whole tile
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < 8; ++k) {
         x[k] *= cs;
         mx = fmaxf(mx, x[k]);
       }
     } else {
-      // position tq = 32 sp + 4 h + (8 (k / 4) + k % 4) is visible when it is
-      // below both tlim and lim - tpos0
-      const int kvis = min(tlim, lim_now() - tpos0) - (32 * sp + 4 * (lane_now() >> 5));
+      // position tq = 32 sp + spos + (8 (k / 4) + k % 4) is visible when it
+      // is below both tlim and lim - tpos0
+      const int kvis = min(tlim, lim_now() - tpos0) - (32 * sp + spos_now());
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < 8; ++k) {
         x[k] = 8 * (k >> 2) + (k & 3) < kvis ? x[k] * cs : kNegInf;
         mx = fmaxf(mx, x[k]);
       }
     }
-    mx = max32(mx);                                   // the block's maximum
+    mx = max16(max32(mx));                            // the block's maximum
     const float f = mx == kNegInf ? kEmptyBlock : floorf(mx);
     const float c0 = 7.f - f;
     float ws = 0.f;
-    int hi[4], lo[4];
+    int hi[2], lo[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       float p4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p4[i] = __builtin_amdgcn_exp2f(x[4 * q + i] + c0);
       ws += (p4[0] + p4[1]) + (p4[2] + p4[3]);
       split4_fp8(p4[0], p4[1], p4[2], p4[3], hi[q], lo[q]);
     }
-    ws = sum32(ws);
-    if (mine) {
-      const uint32_t pa = (uint32_t)(uintptr_t)LDS_PTR(uint8_t, pg_lds + pbase_now());
-      store_p_f8(pa, hi, lo);
-      if (h == 0)
-        store_blk_f8((uint32_t)(uintptr_t)LDS_PTR(float, (float*)&blk[grp][lane_now() & 31] + sp), f, ws);
+    ws = sum16(sum32(ws));
+    {
+      const int row = srow_now();
+      const int pos = spos_now();
+      store_p_f8((uint32_t)(uintptr_t)LDS_PTR(uint8_t, pg_lds + row * kPRB + 32 * sp + pos), hi, lo);
+      if (pos == 0)   // one lane per row: u = 0, h = 0
+        store_blk_f8((uint32_t)(uintptr_t)LDS_PTR(float, (float*)&blk[grp][row] + sp), f, ws);
     }
   };
 
