@@ -129,6 +129,14 @@ def _check_inputs(q, kv_cache, page_table, seq_lens):
         raise MLAError(2, "seq_lens must be contiguous int32 [B]")
 
 
+def _check_out(name, t, dtype, shape, dev):
+    """A caller-supplied output: contiguous, of the kernel's dtype and shape, on dev."""
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+            or t.device != dev:
+        raise MLAError(2, f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                          f"on {dev} (got {t.dtype} {tuple(t.shape)} on {t.device})")
+
+
 def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -153,9 +161,13 @@ def _attend(entry, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, n
         out = torch.empty((B, Q, H, VALUE_DIM), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
+    _check_out("out", out, torch.bfloat16, (B, Q, H, VALUE_DIM), q.device)
+    _check_out("lse", lse, torch.float32, (B, Q, H), q.device)
     need = int(lib.mla_workspace_size(ctypes.byref(p)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and (workspace.device != q.device or not workspace.is_contiguous()):
+        raise MLAError(6, f"workspace must be contiguous on {q.device}")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(getattr(lib, entry)(ctypes.byref(p), q.data_ptr(), kv_cache.data_ptr(),
@@ -216,13 +228,18 @@ def merge(part_out, part_lse, out=None, lse=None):
     if part_out.dtype != torch.bfloat16 or part_lse.dtype != torch.float32 \
             or not part_out.is_contiguous() or not part_lse.is_contiguous():
         raise MLAError(2, "partials must be contiguous (part_out bfloat16, part_lse float32)")
+    dev = part_out.device
+    if dev.type != "cuda" or part_lse.device != dev:
+        raise MLAError(2, "part_out and part_lse must be on the same GPU")
     rows = 1
     for d in lead:
         rows *= int(d)
     if out is None:
-        out = torch.empty(lead + (VALUE_DIM,), dtype=torch.bfloat16, device=part_out.device)
+        out = torch.empty(lead + (VALUE_DIM,), dtype=torch.bfloat16, device=dev)
     if lse is None:
-        lse = torch.empty(lead, dtype=torch.float32, device=part_out.device)
+        lse = torch.empty(lead, dtype=torch.float32, device=dev)
+    _check_out("out", out, torch.bfloat16, lead + (VALUE_DIM,), dev)
+    _check_out("lse", lse, torch.float32, lead, dev)
     _check(lib.mla_merge(part_out.data_ptr(), part_lse.data_ptr(), S, rows, out.data_ptr(),
                          lse.data_ptr(), _stream(part_out.device)))
     return out, lse

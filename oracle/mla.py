@@ -166,17 +166,5 @@ def merge(part_out, part_lse):
     return out, lse
 
 
-def split_fraction_check(ranges, seq_len):
-    """True when the ranges tile [0, seq_len) without gaps or overlaps."""
-    covered = 0
-    for lo, hi in ranges:
-        if hi <= lo:
-            continue
-        if lo != covered:
-            return False
-        covered = hi
-    return covered == seq_len
-
-
 __all__ = ["gather_sequence", "attend", "mla_reference", "mla_partials", "merge",
-           "split_fraction_check", "LATENT_DIM", "VALUE_DIM", "PAGE"]
+           "LATENT_DIM", "VALUE_DIM", "PAGE"]

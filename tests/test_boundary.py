@@ -209,3 +209,32 @@ def test_append_and_scale_validation(lib):
     assert D(FAKE, -1, FAKE, None) == SHAPE
     assert D(FAKE, (1 << 40) + 1, FAKE, None) == SHAPE
     assert D(FAKE, 10, ctypes.c_void_p(0x1002), None) == SHAPE
+
+
+def test_binding_checks_caller_outputs():
+    """The kernels write B*Q*H*512 bf16 and B*Q*H fp32 through raw pointers: a
+    caller-supplied output of the wrong dtype, shape, layout or device is
+    rejected before any call."""
+    import torch
+    dev = torch.device("cpu")
+    good = torch.empty((2, 3, 12, 512), dtype=torch.bfloat16)
+    _lib._check_out("out", good, torch.bfloat16, (2, 3, 12, 512), dev)
+    bad = [
+        torch.empty((2, 3, 12, 512), dtype=torch.float32),          # dtype
+        torch.empty((2, 3, 12, 256), dtype=torch.bfloat16),         # too small
+        torch.empty((2, 3, 512, 12), dtype=torch.bfloat16).transpose(2, 3),   # not contiguous
+        torch.empty((1, 3, 12, 512), dtype=torch.bfloat16),         # batch
+    ]
+    for t in bad:
+        with pytest.raises(mla.MLAError):
+            _lib._check_out("out", t, torch.bfloat16, (2, 3, 12, 512), dev)
+    with pytest.raises(mla.MLAError):
+        _lib._check_out("out", good, torch.bfloat16, (2, 3, 12, 512), torch.device("meta"))
+
+
+def test_merge_rejects_host_partials():
+    import torch
+    po = torch.zeros((2, 4, 512), dtype=torch.bfloat16)
+    pl = torch.zeros((2, 4), dtype=torch.float32)
+    with pytest.raises(mla.MLAError):
+        mla.merge(po, pl)

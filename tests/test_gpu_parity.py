@@ -562,3 +562,18 @@ def test_errors_raise(gpu_lib):
     with pytest.raises(gpu_lib.MLAError):
         gpu_lib.verify(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale, 1.0,
                        num_splits=4, workspace=ws)
+    # caller-supplied outputs of the wrong dtype, shape or device
+    for kw in (dict(out=torch.empty((1, 1, 12, 512), dtype=torch.float32, device="cuda")),
+               dict(out=torch.empty((1, 1, 12, 256), dtype=torch.bfloat16, device="cuda")),
+               dict(out=torch.empty((1, 1, 12, 512), dtype=torch.bfloat16)),
+               dict(lse=torch.empty((1, 1, 12), dtype=torch.bfloat16, device="cuda")),
+               dict(lse=torch.empty((1, 1, 6), dtype=torch.float32, device="cuda"))):
+        with pytest.raises(gpu_lib.MLAError):
+            gpu_lib.verify(inp.q, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale, 1.0,
+                           **kw)
+    po = torch.zeros((2, 1, 1, 12, 512), dtype=torch.bfloat16, device="cuda")
+    pl = torch.zeros((2, 1, 1, 12), dtype=torch.float32, device="cuda")
+    with pytest.raises(gpu_lib.MLAError):
+        gpu_lib.merge(po, pl, out=torch.empty((1, 1, 12, 512), dtype=torch.float32, device="cuda"))
+    with pytest.raises(gpu_lib.MLAError):
+        gpu_lib.merge(po, pl.cpu())
