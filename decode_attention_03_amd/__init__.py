@@ -20,12 +20,15 @@ from ._lib import (
     num_splits,
     split,
     verify,
+    verify_static,
     workspace_size,
+    STATIC_SCRATCH_BYTES,
 )
 from .build import LIB_PATH
 
 __all__ = [
     "EXPORTS", "MLAError", "MLA_KV_BF16", "MLA_KV_FP8_E4M3", "Params", "decode", "kv_append",
     "kv_dynamic_scale", "load",
-    "make_params", "merge", "num_splits", "split", "verify", "workspace_size", "LIB_PATH",
+    "make_params", "merge", "num_splits", "split", "verify", "verify_static", "workspace_size",
+    "STATIC_SCRATCH_BYTES", "LIB_PATH",
 ]

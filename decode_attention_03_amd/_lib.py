@@ -21,11 +21,13 @@ VALUE_DIM = 512
 _STATUS_NAMES = {
     0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_SHAPE", 3: "MLA_ERR_BAD_DTYPE",
     4: "MLA_ERR_BAD_SCALE", 5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_HIP",
+    8: "MLA_ERR_SCRATCH_LIMIT",
 }
+STATIC_SCRATCH_BYTES = 96 << 20   # MLA_STATIC_SCRATCH_BYTES
 
 # Every symbol include/mla.h declares.
-EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_verify", "mla_split",
-           "mla_merge", "mla_kv_append", "mla_kv_dynamic_scale", "mla_status_string",
+EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_verify", "mla_verify_static",
+           "mla_split", "mla_merge", "mla_kv_append", "mla_kv_dynamic_scale", "mla_status_string",
            "mla_last_hip_error")
 
 
@@ -71,6 +73,8 @@ def load(path=None):
         fn = getattr(lib, name)
         fn.argtypes = [pp, vp, vp, vp, vp, f32, f32, vp, vp, vp, sz, vp]
         fn.restype = i32
+    lib.mla_verify_static.argtypes = [pp, vp, vp, vp, vp, f32, f32, vp, vp, vp]
+    lib.mla_verify_static.restype = i32
     lib.mla_split.argtypes = [pp, vp, vp, vp, vp, f32, f32, vp, vp, vp]
     lib.mla_split.restype = i32
     lib.mla_merge.argtypes = [vp, vp, i32, ctypes.c_int64, vp, vp, vp]
@@ -189,6 +193,28 @@ def verify(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_s
     """mla_verify: Q query tokens with the causal rule.  Returns (out, lse)."""
     return _attend("mla_verify", q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale,
                    num_splits, max_seq_len_hint, out, lse, workspace)
+
+
+def verify_static(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
+                  max_seq_len_hint=0, out=None, lse=None):
+    """mla_verify_static: as verify, with the split partials in the library's static
+    per-GPU array instead of a workspace (the C call allocates nothing).  Calls
+    that overlap in time on one GPU race on that array."""
+    lib = load()
+    _check_inputs(q, kv_cache, page_table, seq_lens)
+    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
+    B, Q, H, _ = q.shape
+    if out is None:
+        out = torch.empty((B, Q, H, VALUE_DIM), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
+    _check_out("out", out, torch.bfloat16, (B, Q, H, VALUE_DIM), q.device)
+    _check_out("lse", lse, torch.float32, (B, Q, H), q.device)
+    _check(lib.mla_verify_static(ctypes.byref(p), q.data_ptr(), kv_cache.data_ptr(),
+                                 page_table.data_ptr(), seq_lens.data_ptr(), float(softmax_scale),
+                                 float(kv_scale), out.data_ptr(), lse.data_ptr(),
+                                 _stream(q.device)))
+    return out, lse
 
 
 def split(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_common.hpp"
@@ -130,9 +131,54 @@ mla_status hip_status(hipError_t e) {
   return MLA_ERR_HIP;
 }
 
+}  // namespace
+
+// Partials of mla_verify_static: one array per GPU the library runs on, held
+// until the process ends.  Host code never uses this name as an address (on
+// the host it is only a stand-in for the symbol); static_scratch() looks up
+// each device's copy with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[MLA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the static partials array on the device of `stream`
+// (looked up once per device, with that device current).
+mla_status static_scratch(hipStream_t stream, void** ptr) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e);
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+// One attention call: split launch (+ merge when S > 1).  With static_ws the
+// partials go to the static array instead of the caller's workspace.
 mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
                   const int32_t* pt, const int32_t* sl, float softmax_scale, float kv_scale,
-                  void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                  void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
+                  bool static_ws = false) {
   mla_status st = check_params(p, max_q);
   if (st != MLA_OK) return st;
   if (!q || !kv || !pt || !sl || !out || !lse) return MLA_ERR_NULL_ARG;
@@ -148,7 +194,13 @@ mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
     return hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, true, s));
   }
   const size_t need = partial_bytes(p, S);
-  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  if (static_ws) {
+    if (need > MLA_STATIC_SCRATCH_BYTES) return MLA_ERR_SCRATCH_LIMIT;
+    st = static_scratch(s, &ws);
+    if (st != MLA_OK) return st;
+  } else if (!ws || ws_bytes < need) {
+    return MLA_ERR_WORKSPACE;
+  }
   const size_t rows = rows_of(p) * (size_t)S;
   a.part_out = (uint16_t*)ws;
   a.part_lse = (float*)((char*)ws + align256(rows * mla::kValue * sizeof(uint16_t)));
@@ -193,6 +245,13 @@ mla_status mla_verify(const mla_params* p, const void* q, const void* kv_cache,
                       size_t workspace_bytes, void* stream) {
   return attend(p, mla::kMaxQ, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, out,
                 lse, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_verify_static(const mla_params* p, const void* q, const void* kv_cache,
+                             const int32_t* page_table, const int32_t* seq_lens, float softmax_scale,
+                             float kv_scale, void* out, float* lse, void* stream) {
+  return attend(p, mla::kMaxQ, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, out,
+                lse, nullptr, 0, stream, true);
 }
 
 mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
@@ -270,6 +329,8 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_UNSUPPORTED: return "request not supported by this library";
     case MLA_ERR_WORKSPACE: return "workspace missing or smaller than mla_workspace_size()";
     case MLA_ERR_HIP: return "HIP runtime error (see mla_last_hip_error)";
+    case MLA_ERR_SCRATCH_LIMIT:
+      return "partials exceed the static scratch of mla_verify_static (MLA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

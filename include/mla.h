@@ -91,8 +91,12 @@ typedef enum {
   MLA_ERR_BAD_SCALE = 4,    /* softmax_scale not finite, or kv_scale not finite and > 0 */
   MLA_ERR_UNSUPPORTED = 5,  /* valid request this library does not implement */
   MLA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than mla_workspace_size() */
-  MLA_ERR_HIP = 7           /* the HIP runtime reported an error */
+  MLA_ERR_HIP = 7,          /* the HIP runtime reported an error */
+  MLA_ERR_SCRATCH_LIMIT = 8 /* mla_verify_static: partials larger than its static scratch */
 } mla_status;
+
+/* Size of the static device array behind mla_verify_static (96 MiB per GPU). */
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
 
 typedef enum {
   MLA_KV_BF16 = 0,          /* bf16 latents, 1152 bytes per position */
@@ -140,6 +144,27 @@ mla_status mla_verify(const mla_params* p, const void* q, const void* kv_cache,
                       const int32_t* page_table, const int32_t* seq_lens,
                       float softmax_scale, float kv_scale, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_verify without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  It allocates nothing.  The split
+ * partials go to a static device array of MLA_STATIC_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on until the process ends
+ * (its address is looked up once per GPU, on the first call there; the
+ * GPU is the device of `stream`, the current device for the NULL stream).
+ * A call whose partials (mla_workspace_size(p) bytes) exceed the array
+ * returns MLA_ERR_SCRATCH_LIMIT and launches nothing (for example B = 64
+ * sequences of up to 65,536 FP8 positions with Q = 3 and 12 heads need
+ * 75.8 MB at 32 splits and fit).  Every call on one GPU shares that GPU's
+ * array, and the array keeps the last call's contents (the partials are
+ * fully rewritten by each call, nothing needs to start at zero): calls that
+ * overlap in time on one GPU -- on different streams or from different host
+ * threads -- race on it and give undefined results; serialise them.  Same
+ * arguments (minus the workspace), results and other errors as mla_verify. */
+mla_status mla_verify_static(const mla_params* p, const void* q, const void* kv_cache,
+                             const int32_t* page_table, const int32_t* seq_lens,
+                             float softmax_scale, float kv_scale, void* out, float* lse,
+                             void* stream);
 
 /* Split-KV partials only: S = mla_num_splits(p) partial outputs (bf16, RNE of
  * the fp32 result, normalised by their own sums, already multiplied by

@@ -53,8 +53,8 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_status_strings(lib):
-    for s in range(8):
-        assert lib.mla_status_string(s)
+    for s in range(9):
+        assert lib.mla_status_string(s) != b"unknown status"
     assert lib.mla_status_string(99) == b"unknown status"
 
 
@@ -238,3 +238,19 @@ def test_merge_rejects_host_partials():
     pl = torch.zeros((2, 4), dtype=torch.float32)
     with pytest.raises(mla.MLAError):
         mla.merge(po, pl)
+
+
+def test_static_entry_rejects_partials_beyond_its_scratch(lib):
+    """mla_verify_static refuses, before any HIP call, a request whose split
+    partials exceed its static per-GPU array (MLA_STATIC_SCRATCH_BYTES)."""
+    p = params(batch=65535, num_q_tokens=3, num_heads=12, max_seq_len_hint=65536,
+               max_blocks_per_seq=4096, num_splits=8)
+    assert lib.mla_workspace_size(ctypes.byref(p)) > mla.STATIC_SCRATCH_BYTES
+    d = ctypes.c_void_p(16)
+    st = lib.mla_verify_static(ctypes.byref(p), d, d, d, d, ctypes.c_float(0.07),
+                               ctypes.c_float(1.0), d, d, None)
+    assert st == 8, st
+    assert b"static scratch" in lib.mla_status_string(8)
+    # the long-context and B = 64 FP8 workloads fit
+    for kw in (dict(), dict(batch=64, max_seq_len_hint=65536, max_blocks_per_seq=4096)):
+        assert lib.mla_workspace_size(ctypes.byref(params(**kw))) <= mla.STATIC_SCRATCH_BYTES
