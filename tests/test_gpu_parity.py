@@ -179,7 +179,8 @@ def test_fp8_growing_scores(gpu_lib, alpha):
     and for the largest jumps the accumulators are rebased.  The lse bound is
     the absolute 1e-3 while |lse| stays in the workloads' range (ln n + 0.4);
     with alpha = 4 it reaches about 415, where the float32 score sums alone
-    are good to about 1e-5 relative, so there the bound scales with |lse|/32."""
+    are good to about 1e-5 relative, so there the bound scales as
+    1e-3 * max(1, |lse| / 100), the stated reading of the tolerance."""
     _say(f"growing scores alpha={alpha}")
     inp = make_inputs([1000, 3000], 3, 12, "fp8", seed=41, device="cuda")
     kv = inp.kv.view(torch.float8_e4m3fn).float() * inp.kv_scale
@@ -193,10 +194,12 @@ def test_fp8_growing_scores(gpu_lib, alpha):
                 q[b, j, hh] = (alpha * (1 + hh) * lat).to(torch.bfloat16)
     inp.q = q
     ro, rl, _ = oracle_out(inp)
-    lse_tol = 1e-3 * max(1.0, float(np.abs(rl).max()) / 32.0)
+    lse_tol = 1e-3 * max(1.0, float(np.abs(rl).max()) / 100.0)
     for S in (0, 1, 3):
         out, lse = run_verify(gpu_lib, inp, num_splits=S)
-        compare(out, lse, ro, rl, f"alpha={alpha} S={S}", lse_tol=lse_tol)
+        dout, dlse = compare(out, lse, ro, rl, f"alpha={alpha} S={S}", lse_tol=lse_tol)
+        _say(f"  alpha={alpha} S={S}: max|lse| = {np.abs(rl).max():.1f}, bound {lse_tol:.2e}, "
+             f"max|dout|/max|ref| = {dout:.3e}, max|dlse| = {dlse:.3e}")
 
 
 def _dominant_key_inputs(lens, gap_nat, body_std, tied, key_pos, seed):
@@ -273,15 +276,15 @@ def test_fp8_dominant_key_long_sequence_c4_splits(gpu_lib):
     _say(f"  max|dout|/max|ref| = {dout:.3e}, max|dlse| = {dlse:.3e}")
 
 
-def test_c6_dcp8_shaped_sampled(gpu_lib):
+def test_c6_dcp8_shaped(gpu_lib):
+    """The DCP8-shaped workload (96 heads over an eighth of the history), every
+    sequence checked."""
     _say("config c6")
     inp = make_config("c6", device="cuda")
     out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=8192)
-    lens = inp.seq_lens.cpu().numpy()
-    idx = sorted(set(np.random.default_rng(606).choice(inp.batch, size=4, replace=False).tolist())
-                 | {int(np.argmax(lens)), int(np.argmin(lens))})
-    ro, rl, _ = oracle_out(inp, idx)
-    compare(out[idx], lse[idx], ro, rl, f"c6 seqs {idx}")
+    ro, rl, _ = oracle_out(inp)
+    dout, dlse = compare(out, lse, ro, rl, "c6")
+    _say(f"  c6: max|dout|/max|ref| = {dout:.3e}, max|dlse| = {dlse:.3e}")
 
 
 def test_decode_entry_point(gpu_lib):
@@ -318,25 +321,41 @@ def test_c3_spec_verify(gpu_lib):
     compare(out, lse, ro, rl, "c3")
 
 
-def test_c4_fp8_verify_sampled(gpu_lib):
+def test_c4_fp8_verify(gpu_lib):
+    """B = 64 FP8 verify over up to 65,536 positions, every sequence checked."""
     _say("config c4")
     inp = make_config("c4", device="cuda")
     out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=65536)
-    idx = sorted(np.random.default_rng(404).choice(inp.batch, size=8, replace=False).tolist())
-    lens = inp.seq_lens.cpu().numpy()
-    idx = sorted(set(idx) | {int(np.argmax(lens)), int(np.argmin(lens))})
-    ro, rl, _ = oracle_out(inp, idx)
-    compare(out[idx], lse[idx], ro, rl, f"c4 seqs {idx}")
-
-
-@pytest.mark.parametrize("layer", [0, 23])
-def test_c5_long_context_layer(gpu_lib, layer):
-    _say(f"config c5 layer {layer}")
-    inp = make_c5_layer(layer, device="cuda")
-    S = 64
-    out, lse = run_verify(gpu_lib, inp, num_splits=S)
     ro, rl, _ = oracle_out(inp)
-    compare(out, lse, ro, rl, f"c5 layer {layer}")
+    dout, dlse = compare(out, lse, ro, rl, "c4")
+    _say(f"  c4: max|dout|/max|ref| = {dout:.3e}, max|dlse| = {dlse:.3e}")
+
+
+def test_c5_long_context_all_layers(gpu_lib):
+    """All 24 layer caches of the long-context workload at the benchmark's
+    split count (64, a multiple of the 8 chunks per sequence); the tolerance
+    is per layer."""
+    worst = (0.0, 0.0)
+    for layer in range(24):
+        _say(f"config c5 layer {layer}")
+        inp = make_c5_layer(layer, device="cuda")
+        out, lse = run_verify(gpu_lib, inp, num_splits=64)
+        ro, rl, _ = oracle_out(inp)
+        dout, dlse = compare(out, lse, ro, rl, f"c5 layer {layer}")
+        worst = (max(worst[0], dout), max(worst[1], dlse))
+        del inp
+    _say(f"  c5 worst layer: max|dout|/max|ref| = {worst[0]:.3e}, max|dlse| = {worst[1]:.3e}")
+
+
+def test_c5b_long_context_layer(gpu_lib):
+    """One layer of the other reading of the long-context sizes: 4 sequences of
+    142,000 positions each, at the split count the library picks for it."""
+    _say("config c5b layer 0")
+    inp = make_c5_layer(0, device="cuda", name="c5b")
+    out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=142000)
+    ro, rl, _ = oracle_out(inp)
+    dout, dlse = compare(out, lse, ro, rl, "c5b layer 0")
+    _say(f"  c5b: max|dout|/max|ref| = {dout:.3e}, max|dlse| = {dlse:.3e}")
 
 
 def test_split_partials_match_oracle(gpu_lib):
@@ -499,9 +518,10 @@ def test_page_table_permutation_bitwise(gpu_lib):
 
 
 def test_head_padding(gpu_lib):
-    """12 heads vs the same 12 + 4 zero-query heads: the real heads agree (rows are
-    packed token-major, so padding moves heads between MFMA tiles and only the
-    fp32 accumulation order may differ) and both match the oracle."""
+    """12 heads vs the same 12 + 4 zero-query heads: the real heads agree bit for
+    bit (rows are packed token-major, so padding moves a head to another row of
+    the MFMA tiles, but every row is computed from its own query alone) and
+    both match the oracle."""
     inp = make_inputs([100, 900], 3, 12, "fp8", seed=11, device="cuda")
     o12, l12 = run_verify(gpu_lib, inp, num_splits=3)
     q16 = torch.zeros((2, 3, 16, 576), dtype=torch.bfloat16, device="cuda")
@@ -509,9 +529,7 @@ def test_head_padding(gpu_lib):
     o16, l16 = gpu_lib.verify(q16, inp.kv, inp.page_table, inp.seq_lens, inp.softmax_scale,
                               inp.kv_scale, num_splits=3)
     torch.cuda.synchronize()
-    a, c = o16[:, :, :12].float(), o12.float()
-    assert (a - c).abs().max().item() <= 2.0 ** -7 * c.abs().max().item()
-    assert (l16[:, :, :12] - l12).abs().max().item() <= 1e-5
+    assert torch.equal(o16[:, :, :12], o12) and torch.equal(l16[:, :, :12], l12)
     ro, rl, _ = oracle_out(inp)
     compare(o16[:, :, :12].contiguous(), l16[:, :, :12].contiguous(), ro, rl, "H=16 padded")
     compare(o12, l12, ro, rl, "H=12")
