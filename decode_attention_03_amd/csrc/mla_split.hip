@@ -108,6 +108,38 @@ __device__ __forceinline__ WgCoord wg_coord(int num_splits, int batch, int row_b
   return c;
 }
 
+// Buffer resource (four SGPRs: base, stride 0, byte range, flags) of `bytes`
+// bytes at `base`; loads past the range read as zero.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), (uint32_t)kBufferRsrcWord3};
+}
+
+// Wave-wide direct-to-LDS copy: lane i's 16 bytes at byte offset `voffset`
+// of the buffer go to LDS address lds_addr + 16 i (buffer_load_dwordx4 ...
+// lds, LDS base in M0, which is saved and restored around it).  Issued from
+// inline assembly so that the compiler does not see an asynchronous LDS
+// write: it would otherwise wait for every copy in flight (vmcnt(0)) before
+// the next LDS read of any buffer, which takes away the prefetch.  Every
+// wait for these copies is an explicit s_waitcnt vmcnt; the asm has no
+// register outputs besides the saved M0.
+__device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t voffset, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(rsrc), "s"(lds_addr));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, p);
+}
+
 // Workgroup barrier for LDS data written with ds_write: drain this wave's LDS
 // traffic, then s_barrier.  (No memory fence: the direct-to-LDS loads are
 // waited for explicitly with vmcnt, so no blanket vmcnt(0) is wanted here.)
@@ -723,120 +755,27 @@ constexpr int pv_voff(int ct, int e) {
          16 * (4 * (ct >> 1) + 2 * ((ct ^ e) & 1));
 }
 
-// LDS reads of the FP8 kernel's key, value and probability operands are
-// issued from inline assembly, which waits for its own reads before it ends:
-// the compiler would otherwise treat these reads as possibly aliasing the
-// in-flight direct-to-LDS copies of later tiles and wait for all of them
-// (vmcnt(0)), which defeats the copy pipeline.  The copies of the tile being
-// read were waited for explicitly before the barrier that published it.
+// The FP8 kernel issues its tile and query copies with copy16_to_lds, which
+// the compiler does not see as LDS writes, so its key, value and probability
+// reads are ordinary LDS loads that the compiler schedules between the
+// MFMAs (with the copies visible it would wait for all of them before each
+// read).  The copies of the tile being read were waited for explicitly
+// before the barrier that published it.
 
-// Key operand of one k-step: 16 bytes at each of two lane addresses (chunks
-// 4ks + 2h and 4ks + 2h + 1 of the lane's position row).
-template <int OFF>
-__device__ __forceinline__ i32x8 read_k_f8(uint32_t a0, uint32_t a1) {
-  u32x4 v0, v1;
-  asm volatile(
-      "ds_read_b128 %0, %2 offset:%4\n\t"
-      "ds_read_b128 %1, %3 offset:%4\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1)
-      : "v"(a0), "v"(a1), "i"(OFF));
-  return __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-}
-
-// Value offsets of column tiles 0 and 1 (read_v128_f8 checks tiles 2 and 3).
+// Value offsets of column tiles 0 and 1 (tiles 2 and 3 below).
 static_assert(pv_voff(0, 0) == 0 && pv_voff(0, 1) == 4640 && pv_voff(0, 2) == 18432 &&
               pv_voff(0, 3) == 23072 && pv_voff(1, 0) == 32 && pv_voff(1, 1) == 4608 &&
-              pv_voff(1, 2) == 18464 && pv_voff(1, 3) == 23040, "offsets in read_v128_f8");
-
-// Key operands of two consecutive k-steps (offsets OFF and OFF + 64).
-template <int OFF>
-__device__ __forceinline__ void read_k2_f8(uint32_t a0, uint32_t a1, i32x8& k0, i32x8& k1) {
-  u32x4 v0, v1, v2, v3;
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%6\n\t"
-      "ds_read_b128 %1, %5 offset:%6\n\t"
-      "ds_read_b128 %2, %4 offset:%7\n\t"
-      "ds_read_b128 %3, %5 offset:%7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
-      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 64));
-  k0 = __builtin_bit_cast(i32x8, u32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-  k1 = __builtin_bit_cast(i32x8, u32x8{v2[0], v2[1], v2[2], v2[3], v3[0], v3[1], v3[2], v3[3]});
-}
+              pv_voff(1, 2) == 18464 && pv_voff(1, 3) == 23040, "value offsets");
 
 constexpr int kF8Waves = 8;
 constexpr int kF8Threads = kF8Waves * 64;
-
-// LDS reads of the start of an MFMA phase, one round trip: the block data of
-// row r32 ({f0, f1, sum0, sum1}) and the lane's two probability terms, 2560
-// bytes apart, each 16 bytes of position block 0 and 16 of block 1 (lane half
-// h: positions 16h + 0..15 and 32 + 16h + 0..15).
-__device__ __forceinline__ void read_phase_f8(uint32_t baddr, uint32_t paddr, f32x4& bk, i32x8 (&pf)[2]) {
-  u32x4 b, p0, p1, p2, p3;
-  asm volatile(
-      "ds_read_b128 %0, %5\n\t"
-      "ds_read_b128 %1, %6\n\t"
-      "ds_read_b128 %2, %6 offset:32\n\t"
-      "ds_read_b128 %3, %6 offset:2560\n\t"
-      "ds_read_b128 %4, %6 offset:2592\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(b), "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
-      : "v"(baddr), "v"(paddr));
-  bk = __builtin_bit_cast(f32x4, b);
-  pf[0] = __builtin_bit_cast(i32x8, u32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]});
-  pf[1] = __builtin_bit_cast(i32x8, u32x8{p2[0], p2[1], p2[2], p2[3], p3[0], p3[1], p3[2], p3[3]});
-}
-
-// LDS stores of the softmax phase, issued from inline assembly for the same
-// reason: as plain stores the compiler waits for every in-flight copy
-// (vmcnt(0)) before them, and the softmax phase is where group 1 issues the
-// next tile's copies.  The stores have no outputs; the workgroup barrier
-// that ends the phase waits for them (lgkmcnt(0)).
-// Two probability terms of one lane: 4-byte runs at +0 and +8 of the lane's
-// offset, the second term 2560 bytes further.
-__device__ __forceinline__ void store_p_f8(uint32_t addr, const int (&hi)[2], const int (&lo)[2]) {
-  asm volatile(
-      "ds_write2_b32 %0, %2, %3 offset1:2\n\t"
-      "ds_write2_b32 %1, %4, %5 offset1:2"
-      :
-      : "v"(addr), "v"(addr + 2560u), "v"(hi[0]), "v"(hi[1]), "v"(lo[0]), "v"(lo[1]));
-}
-// Block data of one (row, block): f at +0, the weight sum at +8 bytes.
-__device__ __forceinline__ void store_blk_f8(uint32_t addr, float f, float ws) {
-  asm volatile("ds_write2_b32 %0, %1, %2 offset1:2" : : "v"(addr), "v"(f), "v"(ws));
-}
 
 // Value operand of one PV step: column tiles 0..3 (128 columns) x positions
 // 16h + 0..15 and 32 + 16h + 0..15, sixteen transposed reads at the offsets
 // pv_voff(ct, e).
 static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 18496 &&
               pv_voff(2, 3) == 23136 && pv_voff(3, 0) == 96 && pv_voff(3, 1) == 4672 &&
-              pv_voff(3, 2) == 18528 && pv_voff(3, 3) == 23104, "offsets in read_v128_f8");
-__device__ __forceinline__ void read_v128_f8(uint32_t vaddr, u32x2 (&v)[16]) {
-  asm volatile(
-      "ds_read_b64_tr_b8 %0, %16\n\t"
-      "ds_read_b64_tr_b8 %1, %16 offset:4640\n\t"
-      "ds_read_b64_tr_b8 %2, %16 offset:18432\n\t"
-      "ds_read_b64_tr_b8 %3, %16 offset:23072\n\t"
-      "ds_read_b64_tr_b8 %4, %16 offset:32\n\t"
-      "ds_read_b64_tr_b8 %5, %16 offset:4608\n\t"
-      "ds_read_b64_tr_b8 %6, %16 offset:18464\n\t"
-      "ds_read_b64_tr_b8 %7, %16 offset:23040\n\t"
-      "ds_read_b64_tr_b8 %8, %16 offset:64\n\t"
-      "ds_read_b64_tr_b8 %9, %16 offset:4704\n\t"
-      "ds_read_b64_tr_b8 %10, %16 offset:18496\n\t"
-      "ds_read_b64_tr_b8 %11, %16 offset:23136\n\t"
-      "ds_read_b64_tr_b8 %12, %16 offset:96\n\t"
-      "ds_read_b64_tr_b8 %13, %16 offset:4672\n\t"
-      "ds_read_b64_tr_b8 %14, %16 offset:18528\n\t"
-      "ds_read_b64_tr_b8 %15, %16 offset:23104\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-        "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
-        "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
-      : "v"(vaddr));
-}
+              pv_voff(3, 2) == 18528 && pv_voff(3, 3) == 23104, "value offsets");
 
 // A lane's query fragments from the block staged in LDS (see the prologue of
 // split_kernel_f8x64): a[c] is the address of chunk pair c at the lane's
@@ -954,12 +893,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   constexpr float kSlack = 16.f;
   // floor of the maximum of a block with no visible position (its weights are 0)
   constexpr float kEmptyBlock = -1.0e30f;
-  static_assert(kPTerm == 2560, "read_phase_f8 assumes 2560 bytes between the terms");
+  
 
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][2 * kPTerm];   // [group][term][row][position]
-  // partial scores for the partner: 16 per lane of the 32 lanes whose rows it takes
-  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][2][64];
+  // partial scores after the QK exchange (see the MFMA phase): [wave][set][half][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][2][2][64];
   // per group and row: {f of block 0, f of block 1, fp32 weight sum of block 0, of block 1}
   __shared__ __attribute__((aligned(16))) f32x4 blk[2][32];
   __shared__ float qmax[kF8Waves][32];
@@ -974,7 +913,6 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int sp = v4 & 1;
   const int dh = v4 >> 1;
   const int ks0 = dh ? 5 : 0;
-  const int nks = dh ? 4 : 5;
   const int H = a.heads;
   const int R = a.num_q * H;
   const WgCoord wc = wg_coord(a.num_splits, a.batch, (R + 63) / 64);
@@ -990,14 +928,13 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   uint8_t* const qlds = kv_lds + kTileB;
   {
     const int nrows = min(64, R - 64 * wc.z);
-    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.q + ((int64_t)b * R + 64 * wc.z) * kLatent), 0, nrows * 2 * kLatent, kBufferRsrcWord3);
+    const u32x4 qrsrc = buffer_rsrc(a.q + ((int64_t)b * R + 64 * wc.z) * kLatent, nrows * 2 * kLatent);
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
       const int slot = 64 * (w + 8 * i) + lane;   // 16-byte LDS slot of this lane
       const int r = slot / 72, x = slot - 72 * (slot / 72);
       const uint32_t src = 16u * (uint32_t)(72 * r + (x ^ (r & 7)));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, LDS_PTR(void, qlds + 1024 * (w + 8 * i)), 16, src, 0, 0, 0);
+      copy16_to_lds(qrsrc, src, lds_addr(qlds + 1024 * (w + 8 * i)));
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1010,29 +947,44 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int p1 = (split + 1) * pq + ((split + 1) * pr) / S;
   const int ntiles = (p1 - p0 + kTilePages - 1) / kTilePages;
 
+  // An opaque copy of the lane index, taken where a lane-dependent address or
+  // bound is needed inside the loop: derived from it there (one or two VALU
+  // operations), the value does not hold a register of its own across the
+  // loop, where nearly every register is taken.
+  auto lane_now = [&]() -> int {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
   // ---- a2: copies.  Tile T goes to LDS buffer T % 3; wave w copies page
-  // w % 4 (nine wave-wide one-KiB loads from one buffer descriptor).  Tiles 0
-  // and 1 are copied in the prologue: tile 0 by waves 0..3 as soon as its
-  // page-table entries are known, tile 1 by waves 4..7 once every wave has
-  // read the query staged in buffers 1 and 2;
-  // tile T >= 2 is copied by group 1 at E(T - 2), while it runs its softmax,
-  // so the copy issue never sits on the MFMA-role path and two tiles are in
-  // flight.  A page outside the split, or the positions past seq_len in the
-  // last page, lie outside the buffer range and are written to LDS as zeros by
-  // the copy itself.
+  // w % 4 (wave-wide one-KiB loads from one buffer descriptor).  Tiles 0
+  // and 1 are copied in the prologue, whole pages: tile 0 by waves 0..3 as
+  // soon as its page-table entries are known, tile 1 by waves 4..7 once every
+  // wave has read the query staged in buffers 1 and 2.  Each tile T >= 2 is
+  // copied by both groups while they run their softmax, two tiles ahead:
+  // group 1 loads 0..kLoads1-1 of each page at E(T - 2), group 0 the rest at
+  // O(T - 2), so the copy issue never sits on the MFMA-role path and is shared
+  // between the two softmax phases.  A page outside the split, or the
+  // positions past seq_len in the last page, lie outside the buffer range and
+  // are written to LDS as zeros by the copy itself.
   // Page-table entry of page v4 of tile T (entries past the sequence are
-  // clamped to its last page and not used).
-  const int32_t* pt_b = a.page_table + (int64_t)b * a.max_blocks;
+  // clamped to its last page and not used), read through the constant
+  // address space: the index is wave-uniform, so this is a scalar load,
+  // which does not count against vmcnt.
+  constexpr int kLoads1 = 5;   // group 1's share of a page's nine loads
+  const __attribute__((address_space(4))) int32_t* pt_b =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + (int64_t)b * a.max_blocks);
   const int plast = max(P - 1, 0);
   auto pt_load = [&](int T) -> int {
     return pt_b[min(p0 + T * kTilePages + v4, plast)];
   };
-  auto issue_tile = [&](int T, int ptv) {
+  // loads C0 .. C1 - 1 (compile-time range) of page v4 of tile T
+  auto issue_part = [&](int T, int ptv, auto C0, auto C1) {
+    constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value;
     const int gp = p0 + T * kTilePages + v4;
     const int blk = __builtin_amdgcn_readfirstlane(ptv);
     const int bytes = gp < p1 ? min(kPage, L - gp * kPage) * G::kRowB : 0;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB), 0, bytes, kBufferRsrcWord3);
+    const u32x4 rsrc = buffer_rsrc(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB, bytes);
     uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + v4 * G::kPageB;
     // LDS slot s = 64c + lane of the page holds source chunk
     // 36 row + (x ^ swz(row)) with row = s / 36, x = s % 36.  As 36 is a
@@ -1041,17 +993,23 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     // d0 = 64c / 144 and t = 144 (d0 + 1) - 64c known per load: one or three
     // VALU operations per load instead of a division.
     static_assert(G::kChunksPerRow == 36, "FP8 page rows of 36 chunks");
-    const uint32_t vb = 16u * (uint32_t)lane;
+    // derived from an opaque copy of the lane index: hoisted out of the loop,
+    // the offsets would hold registers (or spill) between copies
+    const int ln = lane_now();
+    const uint32_t vb = 16u * (uint32_t)ln;
 #pragma unroll
-    for (int c = 0; c < kWaveLoads; ++c) {
+    for (int c = c0; c < c1; ++c) {
       constexpr int kRowsPerSwz = 4 * G::kChunksPerRow;   // 144 slots per swizzle value
       const int d0 = (64 * c) / kRowsPerSwz;
       const int t = kRowsPerSwz * (d0 + 1) - 64 * c;
-      const uint32_t d = (uint32_t)d0 + ((t < 64 && lane >= t) ? 1u : 0u);
+      const uint32_t d = (uint32_t)d0 + ((t < 64 && ln >= t) ? 1u : 0u);
       const uint32_t voff = (vb + 1024u * (uint32_t)c) ^ (d << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16, voff, 0, 0, 0);
+      copy16_to_lds(rsrc, voff, lds_addr(dst + 1024 * c));
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, kLoads1>;
+  using I9 = std::integral_constant<int, kWaveLoads>;
 
   // ---- query: q * 2^e = q1 + q2 (FP8), dims 64(ks0 + ks) + 32h + j of row `myrow`.
   // The workgroup's 64 query rows (1,152 bytes each) are staged once in KV
@@ -1069,10 +1027,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     const int pt0 = pt_load(grp);
     ptA = pt_load(2);
     ptB = pt_load(3);
+    // The probability terms and block data read by each group's first PV
+    // are zeros (that PV adds nothing; published by the barrier below).
+    for (int i = tid; i < (int)(sizeof(p_lds) / 16); i += kF8Threads) ((u32x4*)p_lds)[i] = u32x4{};
+    if (tid < 64) blk[tid >> 5][tid & 31] = f32x4{kEmptyBlock, kEmptyBlock, 0.f, 0.f};
     // tile 0's copies go out as soon as its page-table entries are known
     // (group 0; buffer 0 is not part of the staged query)
     if (grp == 0) {
-      issue_tile(0, pt0);
+      issue_part(0, pt0, I0{}, I9{});
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));   // this wave's query loads
     } else {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -1100,7 +1062,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     if (h == 0) qmax[w][r32] = mx;
     lds_barrier();   // also: every wave has read the staged query
     if (grp == 1) {
-      issue_tile(1, pt0);
+      issue_part(1, pt0, I0{}, I9{});
       __builtin_amdgcn_sched_barrier(0);
     }
     mx = fmaxf(qmax[w][r32], qmax[w ^ 2][r32]);     // the other half of the dims
@@ -1113,7 +1075,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     q_unscale = pow2f(-e);
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks) {
-      if (ks >= nks) break;   // dh = 1 has four steps
+      // dh = 1 has four steps: its fifth query terms are zeros (qv[4] = 0)
       i32x8 hi8, lo8;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -1148,22 +1110,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   f32x16 o[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) o[c] = f32x16{};
-  i32x8 vfr[4];     // value fragments of the group's next PV
-  // this wave's partial scores kept from QK for the softmax of the next
-  // phase: 8 of one row of 16dh..16dh+15 per lane (see qk)
-  float x[8];
+  i32x8 vfr[4];     // value fragments of the group's next PV (zeros before the first)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vfr[c] = i32x8{};
 
   uint8_t* const pg_lds = p_lds[grp];
 
-  // An opaque copy of the lane index, taken where a lane-dependent address or
-  // bound is needed inside the loop: derived from it there (one or two VALU
-  // operations), the value does not hold a register of its own across the
-  // loop, where nearly every register is taken.
-  auto lane_now = [&]() -> int {
-    int l = lane;
-    asm volatile("" : "+v"(l));
-    return l;
-  };
   // Row (within the group) of the lane's scores in the softmax: 16dh + l % 16.
   auto srow_now = [&]() -> int { return (lane_now() & 15) + 16 * dh; };
   // Causal limit of that row (visible: position < lim), needed on edge tiles
@@ -1190,91 +1142,67 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     return 16 * ((ln >> 4) & 1) + 4 * (ln >> 5);
   };
 
-  // ---- a4: partial S^T over this wave's k-steps, then the value fragments.
-  // Key addresses of tile T for this wave (lane's row, chunk pair 2h, 2h + 1).
-  auto kaddr = [&](int T, uint32_t& kb0, uint32_t& kb1) {
-    const uint8_t* tile = kv_lds + (T % kNBuf) * kTileB;
+  // ---- a4: partial S^T over this wave's k-steps.
+  // Key operand of k-step ks (relative to the wave's first, ks0) of tile T:
+  // 16 bytes at each of chunks 2h and 2h + 1 of the k-step's 64 dims of the
+  // lane's position row (XOR-swizzled within the row's 4-chunk groups).
+  auto kptr = [&](int T) -> const uint8_t* {
     const int ln = lane_now();
     const int prow = ln & 15;
     const int kpage = 2 * sp + ((ln >> 4) & 1);
-    const int hh = ln >> 5;
-    kb0 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * hh, 0) + 64 * ks0);
-    kb1 = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, tile + kpage * G::kPageB + G::off(prow, 2 * hh + 1, 0) + 64 * ks0);
+    return kv_lds + (T % kNBuf) * kTileB + kpage * G::kPageB + G::off(prow, 2 * (ln >> 5), 0) + 64 * ks0;
   };
-  // The value operand for the PV of this tile is read after the last key
-  // operands, while the last score MFMAs drain (the tile is not read after
-  // this phase).  The PV product's K index runs over the tile's 64 positions
-  // so that each 32-index block of its E8M0 scales (bytes 0..15 of both lane
-  // halves, then bytes 16..31 of both) is one position block of the softmax:
-  // lane half h, byte j holds position 32(j/16) + 16h + j%16.  Column tile
-  // ct, bytes 8e .. 8e+7: source lane sl of a 16-lane group reads position
+  // distance from chunk 2h to chunk 2h + 1 after the swizzle: +16 or -16 bytes
+  auto kpair = [&]() -> int {
+    const int ln = lane_now();
+    return ((ln & 15) >> 2) & 1 ? -16 : 16;
+  };
+  auto kop = [&](const uint8_t* kp, int d1, int ks) -> i32x8 {
+    const u32x4 x0 = *(const u32x4*)(kp + 64 * ks);
+    const u32x4 x1 = *(const u32x4*)(kp + 64 * ks + d1);
+    return __builtin_bit_cast(i32x8, u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+  };
+  // Value operand of the PV (read for the next phase once this phase's PV
+  // has used the registers; the tile is not read after this phase).  The PV
+  // product's K index runs over the tile's 64 positions so that each
+  // 32-index block of its E8M0 scales (bytes 0..15 of both lane halves, then
+  // bytes 16..31 of both) is one position block of the softmax: lane half h,
+  // byte j holds position 32(j/16) + 16h + j%16.  Column tile ct, bytes
+  // 8e .. 8e+7: source lane sl of a 16-lane group reads position
   // 32(e/2) + 16h + 8(e%2) + sl/2, i.e. page h + 2(e/2), row 8(e%2) + sl/2,
-  // byte half sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by (row/4)%4 =
-  // sl/8 + 2(e%2); vbase is the lane part of that address and pv_voff(ct, e)
-  // the rest.
-  auto qk = [&](int T) {
-    uint32_t kb0, kb1;
-    kaddr(T, kb0, kb1);
-    const uint32_t vaddr = (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, kv_lds + (T % kNBuf) * kTileB + vbase_now());
-    f32x16 s = f32x16{};
-    u32x2 vr[16];
-    i32x8 ka, kb;
-    read_k2_f8<0>(kb0, kb1, ka, kb);
-    s = mfma_f8(ka, q1[0], s);
-    s = mfma_f8(ka, q2[0], s);
-    s = mfma_f8(kb, q1[1], s);
-    s = mfma_f8(kb, q2[1], s);
-    __builtin_amdgcn_sched_barrier(0);
-    read_k2_f8<128>(kb0, kb1, ka, kb);
-    s = mfma_f8(ka, q1[2], s);
-    s = mfma_f8(ka, q2[2], s);
-    s = mfma_f8(kb, q1[3], s);
-    s = mfma_f8(kb, q2[3], s);
-    __builtin_amdgcn_sched_barrier(0);
-    if (!dh) {
-      ka = read_k_f8<256>(kb0, kb1);
-      s = mfma_f8(ka, q1[4], s);
-      s = mfma_f8(ka, q2[4], s);
+  // byte half sl%2 of chunk 8v + 2ct + (g16%2), XOR-swizzled by
+  // (row/4)%4 = sl/8 + 2(e%2); vbase is the lane part of that address and
+  // pv_voff(ct, e) the rest.
+  auto vread = [&](const uint8_t* vp, int ct) -> i32x8 {
+    u32x2 vr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      vr[e] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vp + pv_voff(ct, e))));
+    return __builtin_bit_cast(i32x8, u32x8{vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]});
+  };
+  // Partial scores to the softmax.  Rows 16dh..16dh+15 are finished by this
+  // wave, the other 16 by the partner (wave w ^ 2, the other dimension
+  // half), 8 scores per lane either way.  Lane l (row l % 32, position half
+  // h) holds elements 0..15 of its row.  One lane swap between lanes l and
+  // l ^ 16 per element pair (k, k + 8) gives set 0 (the lanes of rows 0..15
+  // with their elements 0..7, the lanes of rows 16..31 with elements 8..15 of
+  // row (l % 32) - 16: rows 0..15) and set 1 (rows 16..31 likewise); both
+  // sets go to LDS, and the softmax of wave w adds set dh of wave w and of
+  // its partner.
+  auto send_scores = [&](const f32x16& s) {
+    uint32_t r0[8], r1[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[k]), __float_as_uint(s[k + 8]),
+                                                      false, false);
+      r0[k] = r[0];
+      r1[k] = r[1];
     }
-    __builtin_amdgcn_sched_barrier(0);
-    read_v128_f8(vaddr, vr);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      vfr[ct] = __builtin_bit_cast(i32x8, u32x8{vr[4 * ct][0], vr[4 * ct][1], vr[4 * ct + 1][0],
-                                                vr[4 * ct + 1][1], vr[4 * ct + 2][0], vr[4 * ct + 2][1],
-                                                vr[4 * ct + 3][0], vr[4 * ct + 3][1]});
-    // Rows 16dh..16dh+15 stay with this wave, the other 16 go to the
-    // partner, 8 scores per lane either way.  Lane l (row l % 32, position
-    // half h) holds elements 0..15 of its row.  One lane swap between lanes
-    // l and l ^ 16 per element pair (k, k + 8) leaves in every lane 8 values
-    // to keep and 8 to send; the partner's lane l keeps the sent ones.  With
-    // dh = 0 the lanes of rows 0..15 keep their elements 0..7 and the lanes
-    // of rows 16..31 elements 8..15 of row (l % 32) - 16; with dh = 1 the
-    // lanes of rows 16..31 keep their elements 8..15 and the lanes of rows
-    // 0..15 elements 0..7 of row (l % 32) + 16.
-    {
-      uint32_t r0[8], r1[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[k]), __float_as_uint(s[k + 8]),
-                                                        false, false);
-        r0[k] = r[0];
-        r1[k] = r[1];
-      }
-      const int ln = lane_now();
-      if (dh) {
-        xbuf[w][0][ln] = __builtin_bit_cast(f32x4, u32x4{r0[0], r0[1], r0[2], r0[3]});
-        xbuf[w][1][ln] = __builtin_bit_cast(f32x4, u32x4{r0[4], r0[5], r0[6], r0[7]});
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = __uint_as_float(r1[k]);
-      } else {
-        xbuf[w][0][ln] = __builtin_bit_cast(f32x4, u32x4{r1[0], r1[1], r1[2], r1[3]});
-        xbuf[w][1][ln] = __builtin_bit_cast(f32x4, u32x4{r1[4], r1[5], r1[6], r1[7]});
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = __uint_as_float(r0[k]);
-      }
-    }
+    const int ln = lane_now();
+    xbuf[w][0][0][ln] = __builtin_bit_cast(f32x4, u32x4{r0[0], r0[1], r0[2], r0[3]});
+    xbuf[w][0][1][ln] = __builtin_bit_cast(f32x4, u32x4{r0[4], r0[5], r0[6], r0[7]});
+    xbuf[w][1][0][ln] = __builtin_bit_cast(f32x4, u32x4{r1[0], r1[1], r1[2], r1[3]});
+    xbuf[w][1][1][ln] = __builtin_bit_cast(f32x4, u32x4{r1[4], r1[5], r1[6], r1[7]});
   };
 
   // ---- a5: partner's partial scores added, scale to log2 units, mask (edge
@@ -1283,14 +1211,17 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // 16dh + l % 16; lanes l, l ^ 16, l ^ 32 and l ^ 48 together hold the
   // row's whole block.
   auto softmax = [&](int T) {
+    float x[8];
     {
       const int ln = lane_now();
-      const f32x4 u0 = xbuf[w ^ 2][0][ln];
-      const f32x4 u1 = xbuf[w ^ 2][1][ln];
+      const f32x4 a0 = xbuf[w][dh][0][ln];
+      const f32x4 a1 = xbuf[w][dh][1][ln];
+      const f32x4 u0 = xbuf[w ^ 2][dh][0][ln];
+      const f32x4 u1 = xbuf[w ^ 2][dh][1][ln];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        x[k] += u0[k];
-        x[4 + k] += u1[k];
+        x[k] = a0[k] + u0[k];
+        x[4 + k] = a1[k] + u1[k];
       }
     }
     const int tpos0 = (p0 + T * kTilePages) * kPage;
@@ -1329,20 +1260,30 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     {
       const int row = srow_now();
       const int pos = spos_now();
-      store_p_f8((uint32_t)(uintptr_t)LDS_PTR(uint8_t, pg_lds + row * kPRB + 32 * sp + pos), hi, lo);
-      if (pos == 0)   // one lane per row: u = 0, h = 0
-        store_blk_f8((uint32_t)(uintptr_t)LDS_PTR(float, (float*)&blk[grp][row] + sp), f, ws);
+      uint8_t* const pp = pg_lds + row * kPRB + 32 * sp + pos;
+      *(int*)pp = hi[0];
+      *(int*)(pp + 8) = hi[1];
+      *(int*)(pp + kPTerm) = lo[0];
+      *(int*)(pp + kPTerm + 8) = lo[1];
+      if (pos == 0) {   // one lane per row: u = 0, h = 0
+        float* const bp = (float*)&blk[grp][row];
+        bp[sp] = f;
+        bp[2 + sp] = ws;
+      }
     }
   };
 
-  // Start of an MFMA phase: the reference maximum of the lane's row moves to
-  // the tile maximum when that passes it by more than 2^kSlack (O and l are
-  // rescaled by the exact power of two), then the E8M0 codes of the two
-  // blocks against it, 127 + f - 7 - mref (at least 0: a block more than
+  // Reference maximum of the lane's row, checked in each MFMA phase: it
+  // moves to the tile maximum when that passes it by more than 2^kSlack (O
+  // and l are rescaled by the exact power of two), then the E8M0 codes of the
+  // two blocks against it, 127 + f - 7 - mref (at least 0: a block more than
   // 2^120 below the reference weighs at most 2^-119 of it), and the row sum
   // of the tile under the same codes.  Returns the code of the lane's own
-  // block (the B operand's scale of its PV lane).
-  auto rebase = [&](const f32x4 bk) -> int {
+  // block (the B operand's scale of its PV lane).  `s` is the score
+  // accumulator of the MFMAs issued before the check: named in the (rarely
+  // taken) rescale branch so that the compiler keeps those MFMAs ahead of the
+  // branch instead of moving them to the join, where they would wait for it.
+  auto rebase = [&](const f32x4 bk, const f32x16& s) -> int {
     const float tm = fmaxf(bk[0], bk[1]);
     const bool mv = tm > mref + kSlack;
     const float mn = mv ? tm : mref;
@@ -1353,6 +1294,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       o[1] *= alpha;
       o[2] *= alpha;
       o[3] *= alpha;
+      asm volatile("" ::"v"(s));
     }
     mref = mn;
     const int e0 = (int)fminf(fmaxf(120.f + bk[0] - mn, 0.f), 254.f);
@@ -1361,65 +1303,120 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     return h ? e1 : e0;
   };
 
-  // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127,
-  // with the block's E8M0 scale on operand B.
-  auto pv = [&](int e, const i32x8 (&pf)[2]) {
-    // written out: a rolled loop here makes the compiler rotate the four
-    // accumulators through one register window with moves
-    o[0] = mfma_f8s(vfr[0], pf[0], o[0], e);
-    o[1] = mfma_f8s(vfr[1], pf[0], o[1], e);
-    o[2] = mfma_f8s(vfr[2], pf[0], o[2], e);
-    o[3] = mfma_f8s(vfr[3], pf[0], o[3], e);
-    o[0] = mfma_f8s(vfr[0], pf[1], o[0], e);
-    o[1] = mfma_f8s(vfr[1], pf[1], o[1], e);
-    o[2] = mfma_f8s(vfr[2], pf[1], o[2], e);
-    o[3] = mfma_f8s(vfr[3], pf[1], o[3], e);
-  };
-
   // Half-steps hs = 0, 1, ...: E(i) = 2i, O(i) = 2i + 1.  Group 0 runs
-  // MFMA(T) (PV of tile T - 1, QK of tile T) at hs = 2T and softmax(T) at
+  // MFMA(T) (QK of tile T, PV of tile T - 1) at hs = 2T and softmax(T) at
   // 2T + 1; group 1 one half-step later, after an idle first one.  Each
-  // group's loop holds one MFMA phase and one softmax phase, so the partial
-  // scores passed from QK to the softmax are dead across iterations.  Both
-  // groups start 2 ntiles + 2 half-steps, each with one workgroup barrier.
-  // Tile 0 (group 0's prologue copies) has landed before the loop; tile 1
-  // (group 1's) only before E(1).
-  // Start of a half-step.  Group 1 copies at every even one (hs = 0 and the
-  // starts of its softmax phases): its vector-memory order is copies(1),
-  // PT(4), copies(2), PT(5), copies(3) ...; before E(T), T >= 1, copies(T)
-  // must have landed while PT(T + 3) and copies(T + 1) may still be in flight.
+  // group's loop holds one MFMA phase and one softmax phase; the partial
+  // scores pass from QK to the softmax through LDS.  Both groups start
+  // 2 ntiles + 2 half-steps, each with one workgroup barrier.  Tile 0 (group
+  // 0's prologue copies) has landed before the loop; tile 1 (group 1's) only
+  // before E(1).
+  // Start of a half-step.  Group 1 copies at even half-steps (hs = 0 and the
+  // starts of its softmax phases), group 0 at odd ones (its softmax phases).
+  // A group's vector-memory order is its share of tiles 2, 3, 4 ... (group
+  // 1: tile 1 whole before them): before E(T), T >= 1, its share of tile T
+  // must have landed while that of tile T + 1 may still be in flight.  The
+  // page-table entries are scalar loads, requested two tiles ahead.
   auto begin = [&](int hs) {
-    const bool copier = grp == 1 && (hs & 1) == 0;
-    if (copier && hs >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads + 1));
+    if ((hs & 1) == 0 && hs >= 2) {
+      if (grp) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
+    }
     lds_barrier();
-    if (copier) {
+    if ((hs & 1) == 1 - grp) {
       const int it = hs >> 1;
       const int cur = (it & 1) ? ptB : ptA;
       const int nxt = pt_load(it + 4);
-      asm volatile("" ::: "memory");   // keep PT(it + 4) ahead of the copies
-      issue_tile(it + 2, cur);
-      // use the new entry only after the copies are issued: waiting for it
-      // then leaves them in flight
-      __builtin_amdgcn_sched_barrier(0);
+      if (grp) issue_part(it + 2, cur, I0{}, I1{});
+      else issue_part(it + 2, cur, I1{}, I9{});
       if (it & 1) ptB = nxt;
       else ptA = nxt;
     }
   };
-  // MFMA role: one LDS round trip for the block data and the PV's
-  // probabilities (stale data where unused); the phase's critical path, so
-  // its instructions go first on the SIMD it shares with a softmax-role wave.
-  auto mfma_phase = [&](int T, bool with_qk) {
+  // MFMA role, the phase's critical path (its instructions go first on the
+  // SIMD it shares with a softmax-role wave).  The block data, the PV's
+  // probability terms and the first two key operands are requested at the
+  // start; the score MFMAs run first (they need only the keys), the
+  // reference maximum is checked while they run, then the PV MFMAs of the
+  // previous tile, column tile by column tile, each followed by the value
+  // reads of this tile into the registers it has just consumed, with the
+  // score exchange between them.  PV and QK run in every MFMA phase: at T = 0
+  // the probability terms, block data and value fragments are zeros (PV adds
+  // nothing), and past the last tile QK reads a stale buffer and its results
+  // are never used.
+  // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127,
+  // with the block's E8M0 scale on operand B.
+  auto mfma_phase = [&](int T) {
     __builtin_amdgcn_s_setprio(2);
-    f32x4 bk;
+    const int ln = lane_now();
+    const int row = ln & 31;
+    const f32x4 bk = blk[grp][row];
+    const uint8_t* kp = kptr(T);
+    const int d1 = kpair();
+    i32x8 ka = kop(kp, d1, 0);
+    i32x8 kb = kop(kp, d1, 1);
     i32x8 pf[2];
     {
-      const int ln = lane_now();
-      read_phase_f8((uint32_t)(uintptr_t)LDS_PTR(const f32x4, &blk[grp][ln & 31]),
-                    (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, pg_lds + (ln & 31) * kPRB + 16 * (ln >> 5)),
-                    bk, pf);
+      const uint8_t* pp = pg_lds + row * kPRB + 16 * (ln >> 5);
+      const u32x4 a0 = *(const u32x4*)pp;
+      const u32x4 a1 = *(const u32x4*)(pp + 32);
+      const u32x4 b0 = *(const u32x4*)(pp + kPTerm);
+      const u32x4 b1 = *(const u32x4*)(pp + kPTerm + 32);
+      pf[0] = __builtin_bit_cast(i32x8, u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+      pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
     }
-    if (T >= 1) pv(rebase(bk), pf);
-    if (with_qk) qk(T);
+    f32x16 s = f32x16{};
+    s = mfma_f8(ka, q1[0], s);
+    s = mfma_f8(ka, q2[0], s);
+    const int e = rebase(bk, s);
+    ka = kop(kp, d1, 2);
+    s = mfma_f8(kb, q1[1], s);
+    s = mfma_f8(kb, q2[1], s);
+    kb = kop(kp, d1, 3);
+    s = mfma_f8(ka, q1[2], s);
+    s = mfma_f8(ka, q2[2], s);
+    // the dh = 1 waves have four k-steps: their fifth reuses the fourth's
+    // keys against zero query terms (no branch, so the phase is one block;
+    // the dh = 0 waves on the other SIMDs run five steps anyway)
+    ka = kop(kp, d1, dh ? 3 : 4);
+    s = mfma_f8(kb, q1[3], s);
+    s = mfma_f8(kb, q2[3], s);
+    s = mfma_f8(ka, q1[4], s);
+    s = mfma_f8(ka, q2[4], s);
+    const uint8_t* vp = kv_lds + (T % kNBuf) * kTileB + vbase_now();
+    // written out: a rolled loop here makes the compiler rotate the four
+    // accumulators through one register window with moves
+    o[0] = mfma_f8s(vfr[0], pf[0], o[0], e);
+    o[0] = mfma_f8s(vfr[0], pf[1], o[0], e);
+    vfr[0] = vread(vp, 0);
+    o[1] = mfma_f8s(vfr[1], pf[0], o[1], e);
+    o[1] = mfma_f8s(vfr[1], pf[1], o[1], e);
+    vfr[1] = vread(vp, 1);
+    send_scores(s);
+    o[2] = mfma_f8s(vfr[2], pf[0], o[2], e);
+    o[2] = mfma_f8s(vfr[2], pf[1], o[2], e);
+    vfr[2] = vread(vp, 2);
+    o[3] = mfma_f8s(vfr[3], pf[0], o[3], e);
+    o[3] = mfma_f8s(vfr[3], pf[1], o[3], e);
+    vfr[3] = vread(vp, 3);
+    // Order after the rescale check: each k-step's key reads two MFMAs ahead
+    // of their use, then the PV pairs with each column tile's value reads after it
+    // and the score exchange's LDS writes in the middle.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // keys, step 2
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // QK, step 1
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // keys, step 3
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // QK, step 2
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // keys, step 4
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // QK, steps 3 and 4
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV, column tile 0
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 0
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV 1
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 1
+    __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);   // scores to LDS
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV 2
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 2
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV 3
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 3
     __builtin_amdgcn_s_setprio(0);
   };
   if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -1427,8 +1424,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     begin(hs);
     const int st = hs - grp;
     if (st >= 0 && (st & 1) == 0) {
-      const int T = st >> 1;
-      mfma_phase(T, T < ntiles);
+      mfma_phase(st >> 1);
     } else if (st >= 1) {
       const int T = (st - 1) >> 1;
       if (T < ntiles) softmax(T);
