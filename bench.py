@@ -18,7 +18,6 @@ bounded sample of the same workload.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,7 +29,15 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode KV-read GB/s (% of 8 TB/s HBM) + µs per layer-step, 12 heads"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-SPLIT_SRC = os.path.join(ROOT, "decode_attention_03_amd", "csrc", "mla_split.hip")
+DEVICE_CODE = os.path.join(ROOT, "decode_attention_03_amd", "_build", "device_code.json")
+
+
+def _split_device_sha256():
+    """sha256 of the split kernels' gfx950 assembly in the current build (written
+    by the build next to the objects), or None if the build did not record it."""
+    if not os.path.exists(DEVICE_CODE):
+        return None
+    return json.load(open(DEVICE_CODE)).get("mla_split.hip")
 
 
 def _log(msg):
@@ -79,18 +86,18 @@ def _layers(cfg, device):
     return layers, c
 
 
-def _traffic(tag, num_splits):
-    """HBM bytes per split-kernel launch from the committed counter summary, or
-    None when the summary is missing or was taken on another kernel source or
-    split count."""
+def _profile_record(tag, num_splits):
+    """The committed counter summary of the split kernel for this workload, or
+    None when it is missing or was taken on other split-kernel device code (the
+    gfx950 assembly of the current build) or another split count."""
     path = os.path.join(PROFILES, f"split_traffic__{tag}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src_hash = hashlib.sha256(open(SPLIT_SRC, "rb").read()).hexdigest()
-    if rec.get("split_source_sha256") != src_hash or rec.get("num_splits") != num_splits:
+    dev = _split_device_sha256()
+    if dev is None or rec.get("split_device_sha256") != dev or rec.get("num_splits") != num_splits:
         return None
-    return float(rec["hbm_bytes_per_dispatch"])
+    return rec
 
 
 def _read_csvs(folder, suffix):
@@ -135,6 +142,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
     """Writes profiles/kernel_stats__TAG.md, profiles/split_traffic__TAG.json/.md
     from rocprofv3 output of `bench.py --copy-calibration` runs (CPU only)."""
     import workloads
+    if _split_device_sha256() is None:
+        raise SystemExit("build the library first: the summary records the split kernels' "
+                         "device-code hash of the current build")
     stats = _read_csvs(trace_dir, "kernel_stats.csv")
     trace = _read_csvs(trace_dir, "kernel_trace.csv")
     fetch = _read_csvs(fetch_dir, "counter_collection.csv")
@@ -202,7 +212,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
         "workload": tag,
         "config_key": cfg,
         "num_splits": S,
-        "split_source_sha256": hashlib.sha256(open(SPLIT_SRC, "rb").read()).hexdigest(),
+        "split_device_sha256": _split_device_sha256(),
         "split_avg_us": round(split_avg_us, 3),
         "merge_avg_us": round(float(merge_stat[0]["AverageNs"]) / 1e3, 3) if merge_stat else None,
         "fetch_kib_per_dispatch": round(spl_f[0], 1),
@@ -275,19 +285,24 @@ def _recorded_splits(folder):
     return None
 
 
-def _cpu_baseline(layers, budget_s):
-    """The float64 oracle on the host cores, on whole layers of the same workload
-    until the time budget is spent; returns the rate in GB/s of algorithmic bytes."""
-    import numpy as np
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_rate(layers, budget_s):
+    """The float64 oracle on whole sequences of the given layers until the time
+    budget is spent: (GB/s of algorithmic bytes, sequences, layers, bytes, seconds)."""
     import oracle
     import workloads
     from workloads import compact_for_oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = None
-    cores = len(os.sched_getaffinity(0))
     done_bytes, t_used, n_layers, n_seqs = 0, 0.0, 0, 0
     for inp in layers:
         for b in range(inp.batch):
@@ -304,12 +319,34 @@ def _cpu_baseline(layers, budget_s):
         n_layers += 1
         if t_used >= budget_s:
             break
-    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s",
-            "cores": int(blas_threads or cores), "kind": "oracle",
-            "sample": f"{n_seqs} sequences over {n_layers} layer(s) of the same workload "
-                      f"({done_bytes / 1e6:.1f} MB of algorithmic bytes, {t_used:.1f} s); "
-                      f"float64 NumPy oracle, BLAS threads={blas_threads}, "
-                      f"host cores visible={cores}"}
+    return done_bytes / t_used / 1e9, n_seqs, n_layers, done_bytes, t_used
+
+
+def _cpu_baseline(layers, budget_s):
+    """The float64 oracle on the host cores, on whole layers of the same workload
+    until the time budget is spent, then on one core (BLAS limited to one
+    thread) for a quarter of the budget; rates in GB/s of algorithmic bytes."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits, blas_threads = None, None
+    cores = len(os.sched_getaffinity(0))
+    rate, n_seqs, n_layers, nbytes, t_used = _oracle_rate(layers, budget_s)
+    out = {"value": round(rate, 4), "unit": "GB/s",
+           "cores": int(blas_threads or cores), "kind": "oracle",
+           "sample": f"{n_seqs} sequences over {n_layers} layer(s) of the same workload "
+                     f"({nbytes / 1e6:.1f} MB of algorithmic bytes, {t_used:.1f} s); "
+                     f"float64 NumPy oracle, BLAS threads={blas_threads}, "
+                     f"host cores visible={cores}",
+           "cpu_model": _cpu_model()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            r1, s1, l1, b1, t1 = _oracle_rate(layers, max(1.0, budget_s / 4))
+        out["single_core"] = {"value": round(r1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{s1} sequence(s), {b1 / 1e6:.1f} MB, {t1:.1f} s, "
+                                        "BLAS limited to one thread"}
+    return out
 
 
 def _rank_merge(mla, first, dev, warmup, steps):
@@ -491,6 +528,10 @@ def main():
     ms_per_step = elapsed * 1e3 / (n_replays * reps)
     _log(f"graph replay: {ms_per_step:.3f} ms per step")
 
+    graph_ms = ms_per_step
+    # the headline is the faster of graph replay and eager issue
+    timing_mode = "graph" if graph_ms <= eager_ms else "eager"
+    ms_per_step = min(graph_ms, eager_ms)
     alg = [workloads.algorithmic_bytes(l.seq_lens.cpu().numpy(), l.num_q, l.heads, l.kv_dtype)
            for l in layers]
     flops = [workloads.algorithmic_flops(l.seq_lens.cpu().numpy(), l.num_q, l.heads)
@@ -518,7 +559,8 @@ def main():
     merge_us = timed(graphs["merge"], n_replays) if S > 1 else 0.0
     split_alg = float(np.mean(alg))     # one split launch processes one layer's batch
     achieved = split_alg / (split_us * 1e-6) / 1e9
-    traffic = _traffic(config_tag(args.config), S)
+    prof = _profile_record(config_tag(args.config), S)
+    traffic = None if prof is None else float(prof["hbm_bytes_per_dispatch"])
     # executed MFMA work of the split kernel (padded rows, two-term fp8 operands)
     fp8 = first.kv_dtype == "fp8"
     rows = first.num_q * first.heads
@@ -545,6 +587,18 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": None if traffic is None else round(traffic),
                     "intensity_flop_per_byte": round(intensity, 1)}
+    # the same figure from the committed kernel trace of this build's split
+    # kernel (rocprofv3 average duration), when there is one
+    roofline["achieved_source"] = "HIP events on the launch stream around graph replays"
+    if prof is not None:
+        p_us = float(prof["split_avg_us"])
+        if roofline["bound"] == "hbm":
+            p_ach = split_alg / (p_us * 1e-6) / 1e9
+        else:
+            p_ach = split_flops / (p_us * 1e-6) / 1e12
+        roofline["achieved_profile"] = round(p_ach, 2)
+        roofline["frac_profile"] = round(p_ach / roofline["peak"], 4)
+        roofline["profile_split_us"] = p_us
 
     line = {
         "metric": METRIC,
@@ -577,9 +631,11 @@ def main():
             "mfma_tflops_algorithmic": round(sum(flops) / (ms_per_step * 1e-3) / 1e12, 2),
             "split_kernel_us": round(split_us, 3),
             "merge_kernel_us": round(merge_us, 3),
-            "timing": f"HIP graph of {reps} step(s) ({reps * n_layers} layer calls) replayed; "
-                      "per-kernel times from graphs of one kernel kind, HIP events on the "
-                      "launch stream",
+            "timing": (f"{timing_mode} (faster of: HIP graph of {reps} step(s) "
+                       f"({reps * n_layers} layer calls) replayed, {graph_ms:.4f} ms; eager "
+                       f"issue of one call per layer, {eager_ms:.4f} ms); per-kernel times "
+                       "from graphs of one kernel kind, HIP events on the launch stream"),
+            "graph_ms_per_step": round(graph_ms, 4),
             "steps_timed": n_replays * reps,
             "eager_ms_per_step": round(eager_ms, 4),
         },

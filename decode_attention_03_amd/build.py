@@ -6,9 +6,13 @@ Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
 selection disabled, and linked into decode_attention_03_amd/libmla_hip.so.
 """
 
+import hashlib
+import json
 import os
+import re
 import subprocess
 import sys
+import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -18,6 +22,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmla_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# sha256 of the gfx950 assembly of each kernel source, written by build()
+DEVICE_CODE_PATH = os.path.join(BUILD_DIR, "device_code.json")
+KERNEL_SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip"]
 
 SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip", "mla_api.cpp"]
 
@@ -47,6 +54,19 @@ def _run(cmd, verbose):
     return out
 
 
+def device_code_sha256(src, verbose=False):
+    """sha256 of the gfx950 assembly hipcc emits for one kernel source, with the
+    per-compilation unit id symbol (the only part that changes from one
+    compile of the same source to the next) normalised.  Host-only edits of a
+    source leave it unchanged, any change of its device code changes it."""
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "dev.s")
+        _run([HIPCC] + FLAGS + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out], verbose)
+        text = open(out).read()
+    text = re.sub(r"__hip_cuid_[0-9a-f]+", "__hip_cuid", text)
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def build(verbose=False):
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -57,8 +77,11 @@ def build(verbose=False):
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmds.append([HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(cmds) + len(KERNEL_SOURCES), 8)) as ex:
+        hashes = [ex.submit(device_code_sha256, k, verbose) for k in KERNEL_SOURCES]
         list(ex.map(lambda c: _run(c, verbose), cmds))
+        json.dump({k: h.result() for k, h in zip(KERNEL_SOURCES, hashes)},
+                  open(DEVICE_CODE_PATH, "w"), indent=1)
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)

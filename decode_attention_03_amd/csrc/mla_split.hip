@@ -710,14 +710,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 
 // ---------------------------------------------------------------------------
 // FP8 KV with 33..64 query rows (speculative verify): the FP8 latents are fed
-// to the 32x32x64 FP8 MFMA as stored, with no decode.  The bf16 side of each
-// product is written as a sum of two FP8 terms:
+// to the 32x32x64 FP8 MFMA as stored, with no decode.  The other operand of
+// each product is written as a sum of two FP8 terms:
 //   query:         q * 2^e = q1 + q2, e chosen per row so max|q * 2^e| is in
 //                  [64, 128); q has 8 significant bits and the residual of the
 //                  first RNE rounding fits the second term, so q1 + q2 equals
 //                  q * 2^e up to 2^-10 absolute, i.e. 2^-16 of the row maximum;
-//   probabilities: p * 2^8 = p1 + p2, accurate to 2^-8 relative (bf16 gives
-//                  2^-9), while the softmax denominator keeps the fp32 p.
+//   probabilities: per (row, 32-position block) x = 2^(s - f + 7) in [0, 256)
+//                  against the block's own floor maximum f, x ~ p1 + p2 with
+//                  |x - (p1 + p2)| <= max(2^-8 x, 2^-10), and the block's
+//                  magnitude restored by the MFMA's E8M0 scale on that operand
+//                  (see split_kernel_f8x64 for the bound on the output); the
+//                  softmax denominator adds the fp32 x.
 // Each product therefore takes two FP8 MFMAs, which cost what one bf16 MFMA of
 // the same shape costs, and no VALU conversion touches the KV stream.
 // Rows are two 32-row tiles (r = j*H + h); wave w owns row tile w/2 and the
@@ -1287,7 +1291,9 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     const float tm = fmaxf(bk[0], bk[1]);
     const bool mv = tm > mref + kSlack;
     const float mn = mv ? tm : mref;
-    if (__any(mv)) {
+    // nothing to rescale while no weight has been added (then O is exactly
+    // zero): the first tiles, whose maxima always move the reference, skip it
+    if (__any(mv && l_run > 0.f)) {
       const float alpha = mv ? __builtin_amdgcn_exp2f(mref - mn) : 1.f;   // integer argument
       l_run *= alpha;
       o[0] *= alpha;
