@@ -11,7 +11,7 @@ import os
 
 import torch
 
-from .build import LIB_PATH
+from .build import DEBUG_LIB_PATH, LIB_PATH
 
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
@@ -28,7 +28,9 @@ STATIC_SCRATCH_BYTES = 96 << 20   # MLA_STATIC_SCRATCH_BYTES
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_verify", "mla_verify_static",
            "mla_split", "mla_merge", "mla_kv_append", "mla_kv_dynamic_scale", "mla_status_string",
-           "mla_last_hip_error")
+           "mla_last_hip_error", "mla_debug_build", "mla_debug_flags")
+# Contract violations reported by the debug build (MLA_DEBUG_* of include/mla.h).
+DEBUG_PAGE_ID, DEBUG_SEQ_SHORT, DEBUG_SEQ_LONG = 1, 2, 4
 
 
 class MLAError(RuntimeError):
@@ -53,16 +55,7 @@ class Params(ctypes.Structure):
 _LIB = None
 
 
-def load(path=None):
-    """Load the HIP library (once).  Raises if it has not been built."""
-    global _LIB
-    if _LIB is not None:
-        return _LIB
-    path = path or LIB_PATH
-    if not os.path.exists(path):
-        raise RuntimeError(f"HIP library {path} is missing; build it with "
-                           "`python -m decode_attention_03_amd.build`")
-    lib = ctypes.CDLL(path)
+def _configure(lib):
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     pp = ctypes.POINTER(Params)
     lib.mla_num_splits.argtypes = [pp]
@@ -87,17 +80,53 @@ def load(path=None):
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_hip_error.argtypes = []
     lib.mla_last_hip_error.restype = i32
-    _LIB = lib
+    lib.mla_debug_build.argtypes = []
+    lib.mla_debug_build.restype = i32
+    lib.mla_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
+    lib.mla_debug_flags.restype = i32
     return lib
 
 
-def _check(status):
+def _open(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is missing; build it with "
+                           "`python -m decode_attention_03_amd.build`")
+    return _configure(ctypes.CDLL(path))
+
+
+def load(path=None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    _LIB = _open(path or LIB_PATH)
+    return _LIB
+
+
+def load_debug():
+    """A handle of the debug build (libmla_hip_debug.so, built with MLA_DEBUG=1),
+    separate from the one load() returns; raises if it has not been built."""
+    return _open(DEBUG_LIB_PATH)
+
+
+def debug_flags(lib, clear=True):
+    """The MLA_DEBUG_* bits the debug library `lib` has reported on the current
+    device (synchronous), cleared afterwards unless clear=False."""
+    v = ctypes.c_uint32(0)
+    _check_lib(lib, lib.mla_debug_flags(ctypes.byref(v), 1 if clear else 0))
+    return int(v.value)
+
+
+def _check_lib(lib, status):
     if status != 0:
-        lib = load()
         msg = lib.mla_status_string(status).decode()
         if status == 7:
             msg += f" (hipError {lib.mla_last_hip_error()})"
         raise MLAError(status, msg)
+
+
+def _check(status):
+    _check_lib(load(), status)
 
 
 def _kv_dtype(kv_cache):

@@ -22,6 +22,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmla_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the same sources with MLA_DEBUG=1: device-side checks of the caller contract
+DEBUG_BUILD_DIR = os.path.join(PKG, "_build_debug")
+DEBUG_LIB_PATH = os.path.join(PKG, "libmla_hip_debug.so")
 # sha256 of the gfx950 assembly of each kernel source, written by build()
 DEVICE_CODE_PATH = os.path.join(BUILD_DIR, "device_code.json")
 KERNEL_SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip"]
@@ -67,26 +70,32 @@ def device_code_sha256(src, verbose=False):
     return hashlib.sha256(text.encode()).hexdigest()
 
 
-def build(verbose=False):
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose=False, debug=False):
+    """Compile every source and link the shared library; returns its path.
+    With debug=True the sources are compiled with MLA_DEBUG=1 into the debug
+    library (libmla_hip_debug.so) instead."""
+    bdir = DEBUG_BUILD_DIR if debug else BUILD_DIR
+    lib = DEBUG_LIB_PATH if debug else LIB_PATH
+    flags = FLAGS + (["-DMLA_DEBUG=1"] if debug else [])
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(len(cmds) + len(KERNEL_SOURCES), 8)) as ex:
-        hashes = [ex.submit(device_code_sha256, k, verbose) for k in KERNEL_SOURCES]
+        hashes = [] if debug else [ex.submit(device_code_sha256, k, verbose) for k in KERNEL_SOURCES]
         list(ex.map(lambda c: _run(c, verbose), cmds))
-        json.dump({k: h.result() for k, h in zip(KERNEL_SOURCES, hashes)},
-                  open(DEVICE_CODE_PATH, "w"), indent=1)
-    tmp = LIB_PATH + ".tmp"
+        if not debug:
+            json.dump({k: h.result() for k, h in zip(KERNEL_SOURCES, hashes)},
+                      open(DEVICE_CODE_PATH, "w"), indent=1)
+    tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

@@ -107,6 +107,7 @@ mla::SplitArgs make_args(const mla_params* p, const void* q, const void* kv, con
   a.num_q = p->num_q_tokens;
   a.heads = p->num_heads;
   a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
   a.num_splits = S;
   const float ks = p->kv_dtype == MLA_KV_FP8_E4M3 ? kv_scale : 1.0f;
   a.score_scale_log2 = (float)((double)softmax_scale * (double)ks * 1.4426950408889634);
@@ -139,15 +140,24 @@ mla_status hip_status(hipError_t e) {
 // each device's copy with hipGetSymbolAddress.
 static __device__ __align__(256) uint8_t scratch[MLA_STATIC_SCRATCH_BYTES];
 
+static_assert(mla::kDbgPageId == MLA_DEBUG_PAGE_ID && mla::kDbgSeqShort == MLA_DEBUG_SEQ_SHORT &&
+                  mla::kDbgSeqLong == MLA_DEBUG_SEQ_LONG,
+              "debug flag bits of the kernels and the C ABI");
+
+// Contract violations found by the kernels of the debug build (kDbg* bits of
+// mla_common.hpp), one word per GPU; read and cleared by mla_debug_flags.
+static __device__ uint32_t debug_flags_word;
+
 namespace {
 
 constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mutex;
+std::mutex g_symbol_mutex;
 void* g_scratch_ptr[kMaxDevices] = {};
+void* g_debug_ptr[kMaxDevices] = {};
 
-// Device address of the static partials array on the device of `stream`
-// (looked up once per device, with that device current).
-mla_status static_scratch(hipStream_t stream, void** ptr) {
+// Device address of a library symbol (`sym` is its host-side handle) on the
+// device of `stream`, looked up once per device with that device current.
+mla_status symbol_address(hipStream_t stream, const void* sym, void* (&cache)[kMaxDevices], void** ptr) {
   int cur = 0, dev = 0;
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_status(e);
@@ -157,20 +167,35 @@ mla_status static_scratch(hipStream_t stream, void** ptr) {
     if (e != hipSuccess) return hip_status(e);
   }
   if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
-  std::lock_guard<std::mutex> lock(g_scratch_mutex);
-  if (!g_scratch_ptr[dev]) {
+  std::lock_guard<std::mutex> lock(g_symbol_mutex);
+  if (!cache[dev]) {
     if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
     void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    e = hipGetSymbolAddress(&p, sym);
     if (dev != cur) {
       const hipError_t e2 = hipSetDevice(cur);
       if (e == hipSuccess) e = e2;
     }
     if (e != hipSuccess) return hip_status(e);
-    g_scratch_ptr[dev] = p;
+    cache[dev] = p;
   }
-  *ptr = g_scratch_ptr[dev];
+  *ptr = cache[dev];
   return MLA_OK;
+}
+
+// Device address of the static partials array on the device of `stream`.
+mla_status static_scratch(hipStream_t stream, void** ptr) {
+  return symbol_address(stream, HIP_SYMBOL(scratch), g_scratch_ptr, ptr);
+}
+
+// Debug build: the flag word of the device of `stream` (release: none).
+mla_status debug_flags_ptr(hipStream_t stream, uint32_t** ptr) {
+  *ptr = nullptr;
+  if constexpr (!mla::kDebug) return MLA_OK;
+  void* p = nullptr;
+  const mla_status st = symbol_address(stream, (const void*)&debug_flags_word, g_debug_ptr, &p);
+  *ptr = (uint32_t*)p;
+  return st;
 }
 
 // One attention call: split launch (+ merge when S > 1).  With static_ws the
@@ -188,6 +213,8 @@ mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
   hipStream_t s = (hipStream_t)stream;
   mla::SplitArgs a = make_args(p, q, kv, pt, sl, softmax_scale, kv_scale, S);
   if (!launches_fit(a, p, S)) return MLA_ERR_UNSUPPORTED;
+  st = debug_flags_ptr(s, &a.debug_flags);
+  if (st != MLA_OK) return st;
   if (S == 1) {
     a.out = (uint16_t*)out;
     a.lse = lse;
@@ -266,6 +293,8 @@ mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
   mla::SplitArgs a = make_args(p, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, S);
   if (mla::split_work_items(a, p->kv_dtype == MLA_KV_FP8_E4M3) > mla::kMaxWorkItems)
     return MLA_ERR_UNSUPPORTED;
+  st = debug_flags_ptr((hipStream_t)stream, &a.debug_flags);
+  if (st != MLA_OK) return st;
   a.part_out = (uint16_t*)part_out;
   a.part_lse = part_lse;
   return hip_status(mla::launch_split(a, p->kv_dtype == MLA_KV_FP8_E4M3, false, (hipStream_t)stream));
@@ -309,6 +338,8 @@ mla_status mla_kv_append(const mla_params* p, const void* kv_new, void* kv_cache
   a.max_blocks = p->max_blocks_per_seq;
   a.num_blocks = p->num_blocks;
   a.kv_scale = fp8 ? kv_scale : 1.f;
+  const mla_status st = debug_flags_ptr((hipStream_t)stream, &a.debug_flags);
+  if (st != MLA_OK) return st;
   return hip_status(mla::launch_append(a, fp8, (hipStream_t)stream));
 }
 
@@ -336,5 +367,21 @@ const char* mla_status_string(int32_t status) {
 }
 
 int32_t mla_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t mla_debug_build(void) { return mla::kDebug ? 1 : 0; }
+
+mla_status mla_debug_flags(uint32_t* flags, int32_t clear) {
+  if (!flags) return MLA_ERR_NULL_ARG;
+  *flags = 0;
+  if constexpr (!mla::kDebug) return MLA_OK;
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(debug_flags_word), sizeof(uint32_t));
+  if (e != hipSuccess) return hip_status(e);
+  if (clear) {
+    const uint32_t zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_flags_word), &zero, sizeof(uint32_t));
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return MLA_OK;
+}
 
 }  // extern "C"

@@ -42,6 +42,8 @@ struct SplitArgs {
   int32_t num_splits;
   float score_scale_log2;     // softmax_scale * kv_scale * log2(e)
   float out_scale;            // kv_scale (value vectors are used undecoded-scale in the MFMA)
+  int32_t num_blocks;         // pool blocks (checked by the debug build only)
+  uint32_t* debug_flags;      // debug build: contract violations found (kDbg* bits)
 };
 
 struct MergeArgs {
@@ -63,7 +65,47 @@ struct AppendArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   float kv_scale;             // fp8 only
+  uint32_t* debug_flags;      // debug build: contract violations found (kDbg* bits)
 };
+
+// Debug build (compiled with MLA_DEBUG=1, as libmla_hip_debug.so): the
+// kernels check the caller contract of the C ABI on the device before any
+// read that depends on it, replace a violating value by one inside its range
+// (so every kernel still runs to its end and touches only caller memory) and
+// report the violation in a flag word (kDbg* bits).  The release build trusts
+// the contract and compiles none of this.
+#ifndef MLA_DEBUG
+#define MLA_DEBUG 0
+#endif
+constexpr bool kDebug = MLA_DEBUG != 0;
+constexpr uint32_t kDbgPageId = 1u;     // a page_table entry read is outside [0, num_blocks)
+constexpr uint32_t kDbgSeqShort = 2u;   // seq_lens[b] < num_q_tokens
+constexpr uint32_t kDbgSeqLong = 4u;    // seq_lens[b] > 16 * max_blocks_per_seq
+
+// Vector-memory atomic OR of the lane's bits into the flag word.
+__device__ __forceinline__ void debug_report(uint32_t* flags, uint32_t bits) {
+  if (bits) atomicOr(flags, bits);
+}
+// seq_lens[b] clamped into [num_q, 16 * max_blocks]
+__device__ __forceinline__ int debug_seq_len(int L, int num_q, int max_blocks, uint32_t* flags) {
+  uint32_t bits = 0;
+  if (L < num_q) {
+    bits |= kDbgSeqShort;
+    L = num_q;
+  }
+  if (L > kPage * max_blocks) {
+    bits |= kDbgSeqLong;
+    L = kPage * max_blocks;
+  }
+  debug_report(flags, bits);
+  return L;
+}
+// a page-table entry clamped into [0, num_blocks)
+__device__ __forceinline__ int debug_page_id(int blk, int num_blocks, uint32_t* flags) {
+  if (blk >= 0 && blk < num_blocks) return blk;
+  debug_report(flags, kDbgPageId);
+  return blk < 0 ? 0 : num_blocks - 1;
+}
 
 // Host launchers (defined next to their kernels).  Return hipSuccess or the
 // launch error.

@@ -43,10 +43,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int b = (int)(row / a.num_q);
   const int j = (int)(row - (int64_t)b * a.num_q);
   const int t = a.seq_lens[b] - a.num_q + j;
-  // a slot outside the page table or the pool is a caller error: nothing is written
-  if (t < 0 || t / kPage >= a.max_blocks) return;
+  // a slot outside the page table or the pool is a caller error: nothing is
+  // written (the debug build also reports it)
+  if (t < 0 || t / kPage >= a.max_blocks) {
+    if constexpr (kDebug) debug_report(a.debug_flags, t < 0 ? kDbgSeqShort : kDbgSeqLong);
+    return;
+  }
   const int blk = a.page_table[(int64_t)b * a.max_blocks + t / kPage];
-  if (blk < 0 || blk >= a.num_blocks) return;
+  if (blk < 0 || blk >= a.num_blocks) {
+    if constexpr (kDebug) debug_report(a.debug_flags, kDbgPageId);
+    return;
+  }
   const int64_t slot = (int64_t)blk * kPage + t % kPage;
   const u32x4 v = *(const u32x4*)(a.kv_new + row * kLatent + 8 * c);
   if constexpr (!FP8) {

@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int split = wc.split;
   const int b = wc.b;
 
-  const int L = a.seq_lens[b];
+  const int L = kDebug ? debug_seq_len(a.seq_lens[b], a.num_q, a.max_blocks, a.debug_flags) : a.seq_lens[b];
   const int P = (L + kPage - 1) / kPage;
   const int p0 = (int)(((int64_t)split * P) / a.num_splits);
   const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
@@ -384,7 +384,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     const int page = p0 + T * TPG + wpage;
     if (page < p1) {
       // one buffer resource per page: the copy is bounds-checked to the page
-      const int blk = __builtin_amdgcn_readfirstlane(pt_row[page]);
+      int blk = __builtin_amdgcn_readfirstlane(pt_row[page]);
+      if constexpr (kDebug) blk = debug_page_id(blk, a.num_blocks, a.debug_flags);
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a.kv + (int64_t)blk * G::kPageB), 0, G::kPageB, kBufferRsrcWord3);
 #pragma unroll
@@ -928,7 +929,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // seq_lens[b] is requested first (a scalar load, waited for below), then
   // the query block's loads go out: they need only the workgroup's
   // coordinates (see the query conversion below for the layout).
-  const int L = a.seq_lens[b];
+  const int L = kDebug ? debug_seq_len(a.seq_lens[b], a.num_q, a.max_blocks, a.debug_flags) : a.seq_lens[b];
   uint8_t* const qlds = kv_lds + kTileB;
   {
     const int nrows = min(64, R - 64 * wc.z);
@@ -986,7 +987,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   auto issue_part = [&](int T, int ptv, auto C0, auto C1) {
     constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value;
     const int gp = p0 + T * kTilePages + v4;
-    const int blk = __builtin_amdgcn_readfirstlane(ptv);
+    int blk = __builtin_amdgcn_readfirstlane(ptv);
+    if constexpr (kDebug) blk = gp < p1 ? debug_page_id(blk, a.num_blocks, a.debug_flags) : 0;
     const int bytes = gp < p1 ? min(kPage, L - gp * kPage) * G::kRowB : 0;
     const u32x4 rsrc = buffer_rsrc(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB, bytes);
     uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + v4 * G::kPageB;

@@ -67,9 +67,13 @@
  *   launch has 256 threads per workgroup and query-row block, 512 for FP8
  *   with more than 32 rows, the merge 128, 256 or 1,024 threads per row for
  *   S <= 8, <= 32 or more).
- * - Caller contract, not checked on the device: num_q_tokens <= seq_lens[b]
- *   <= 16 * max_blocks_per_seq and 0 <= page_table[b][p] < num_blocks for the
- *   pages read.  kv_cache and page_table are only read.
+ * - Caller contract, not checked on the device by the release library:
+ *   num_q_tokens <= seq_lens[b] <= 16 * max_blocks_per_seq and
+ *   0 <= page_table[b][p] < num_blocks for the pages read (paged addressing in
+ *   blocks of 16: "Kimi K2.6 + DFlash on 8x MI300X", section "Technical
+ *   numbers").  The debug build of the library (libmla_hip_debug.so, compiled
+ *   with MLA_DEBUG=1) checks it on the device: see mla_debug_flags.
+ *   kv_cache and page_table are only read.
  * - Concurrent calls on different streams are safe when their outputs and
  *   workspaces do not overlap.
  */
@@ -230,6 +234,30 @@ const char* mla_status_string(int32_t status);
 
 /* HIP error code (hipError_t value) behind the last MLA_ERR_HIP on this thread. */
 int32_t mla_last_hip_error(void);
+
+/* Contract violations reported by the debug build (bits of the flag word). */
+#define MLA_DEBUG_PAGE_ID 1u    /* a page_table entry read is outside [0, num_blocks) */
+#define MLA_DEBUG_SEQ_SHORT 2u  /* seq_lens[b] < num_q_tokens */
+#define MLA_DEBUG_SEQ_LONG 4u   /* seq_lens[b] > 16 * max_blocks_per_seq */
+
+/* 1 if this library is the debug build, else 0.  In the debug build every
+ * kernel of mla_decode, mla_verify, mla_verify_static, mla_split and
+ * mla_kv_append checks the caller contract above on the device, before any
+ * read that depends on it: a seq_lens[b] outside [num_q_tokens,
+ * 16 * max_blocks_per_seq] is clamped into that range and a page-table entry
+ * outside [0, num_blocks) is clamped to the nearest block (mla_kv_append
+ * writes nothing for such a slot), so every kernel runs to its end and
+ * touches only the caller's buffers; the violation is ORed into a flag word
+ * of the device (one per GPU, kept until read).  Results of a call with a
+ * violation are not meaningful. */
+int32_t mla_debug_build(void);
+
+/* Debug build: *flags = the current device's flag word (MLA_DEBUG_* bits
+ * ORed by every call since it was last cleared), cleared when `clear` is
+ * nonzero.  Synchronous: waits for the device's outstanding work (unlike
+ * every other entry point).  Release build: *flags = 0, no HIP call.
+ * Errors: NULL_ARG, HIP. */
+mla_status mla_debug_flags(uint32_t* flags, int32_t clear);
 
 #ifdef __cplusplus
 }

@@ -254,3 +254,17 @@ def test_static_entry_rejects_partials_beyond_its_scratch(lib):
     # the long-context and B = 64 FP8 workloads fit
     for kw in (dict(), dict(batch=64, max_seq_len_hint=65536, max_blocks_per_seq=4096)):
         assert lib.mla_workspace_size(ctypes.byref(params(**kw))) <= mla.STATIC_SCRATCH_BYTES
+
+
+def test_debug_library_exports_and_identifies_itself(lib):
+    """The debug build (MLA_DEBUG=1) exports the same symbols; each library
+    says which build it is, and the release build reports no flags without a
+    HIP call."""
+    dbg = _lib.load_debug()
+    for n in _declared():
+        assert hasattr(dbg, n), n
+    assert dbg.mla_debug_build() == 1
+    assert lib.mla_debug_build() == 0
+    v = ctypes.c_uint32(123)
+    assert lib.mla_debug_flags(ctypes.byref(v), 1) == OK and v.value == 0
+    assert lib.mla_debug_flags(None, 0) == NULL
