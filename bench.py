@@ -54,6 +54,8 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak microbenchmarks (HBM read, MFMA)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (negation) for HBM counter "
                          "calibration")
@@ -346,6 +348,50 @@ def _cpu_baseline(layers, budget_s):
         out["single_core"] = {"value": round(r1, 4), "unit": "GB/s", "cores": 1,
                               "sample": f"{s1} sequence(s), {b1 / 1e6:.1f} MB, {t1:.1f} s, "
                                         "BLAS limited to one thread"}
+    return out
+
+
+def _measured_peaks(dev):
+    """HBM read bandwidth and dense MFMA rate measured on this GPU with the
+    library's microbenchmark kernels (include/mla_peaks.h), HIP events on the
+    launch stream: a 2 GiB read (larger than the 256 MB last-level cache) with
+    plain vector loads and with the split kernels' direct-to-LDS loads, and a
+    stream of independent FP8 / bf16 MFMAs on every SIMD."""
+    import torch
+    from decode_attention_03_amd import _lib
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    wgs = 1024
+    isink = torch.zeros(wgs, dtype=torch.int32, device=dev)
+    fsink = torch.zeros(wgs, dtype=torch.float32, device=dev)
+    cur = torch.cuda.current_stream(dev)
+
+    def best_ms(fn, reps=5):
+        fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            fn()
+            e1.record(cur)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return min(times)
+
+    out = {}
+    for name, mode in (("hbm_read_gbs", _lib.PEAK_READ_VGPR), ("hbm_read_lds_gbs", _lib.PEAK_READ_LDS)):
+        ms = best_ms(lambda: _lib.peak_hbm_read(buf, mode, isink, wgs))
+        out[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf
+    iters = 4096
+    for name, kind, flops in (("mfma_fp8_tflops", _lib.PEAK_MFMA_FP8, 131072),
+                              ("mfma_bf16_tflops", _lib.PEAK_MFMA_BF16, 32768)):
+        ms = best_ms(lambda: _lib.peak_mfma(kind, iters, fsink, wgs))
+        total = wgs * 4 * iters * 4 * flops
+        out[name] = round(total / (ms * 1e-3) / 1e12, 1)
+    out["method"] = ("best of 5 launches, HIP events; read: 2 GiB once, 1024 workgroups of "
+                     "256 threads, 16-byte loads; MFMA: 1024 workgroups x 4 waves x 4 independent "
+                     "accumulators")
     return out
 
 
@@ -654,6 +700,16 @@ def main():
     line["config"]["kv_append"] = _append_leg(mla, first, dev, args.warmup, args.steps)
     if first.heads > 12 and first.heads % 12 == 0:
         line["config"]["rank_merge"] = _rank_merge(mla, first, dev, args.warmup, args.steps)
+    if not args.no_peaks:
+        peaks = _measured_peaks(dev)
+        line["measured_peaks"] = peaks
+        if roofline["bound"] == "hbm":
+            best = max(peaks["hbm_read_gbs"], peaks["hbm_read_lds_gbs"])
+            roofline["measured_peak"] = best
+        else:
+            best = peaks["mfma_fp8_tflops"] if fp8 else peaks["mfma_bf16_tflops"]
+            roofline["measured_peak"] = best
+        roofline["frac_of_measured"] = round(roofline["achieved"] / best, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(layers, args.cpu_seconds)
     if args.copy_calibration:

@@ -29,6 +29,10 @@ STATIC_SCRATCH_BYTES = 96 << 20   # MLA_STATIC_SCRATCH_BYTES
 EXPORTS = ("mla_num_splits", "mla_workspace_size", "mla_decode", "mla_verify", "mla_verify_static",
            "mla_split", "mla_merge", "mla_kv_append", "mla_kv_dynamic_scale", "mla_status_string",
            "mla_last_hip_error", "mla_debug_build", "mla_debug_flags")
+# Every symbol include/mla_peaks.h declares (measured-peak microbenchmarks).
+PEAK_EXPORTS = ("mla_peak_hbm_read", "mla_peak_mfma")
+PEAK_READ_VGPR, PEAK_READ_LDS = 0, 1
+PEAK_MFMA_FP8, PEAK_MFMA_BF16 = 0, 1
 # Contract violations reported by the debug build (MLA_DEBUG_* of include/mla.h).
 DEBUG_PAGE_ID, DEBUG_SEQ_SHORT, DEBUG_SEQ_LONG = 1, 2, 4
 
@@ -84,6 +88,10 @@ def _configure(lib):
     lib.mla_debug_build.restype = i32
     lib.mla_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
     lib.mla_debug_flags.restype = i32
+    lib.mla_peak_hbm_read.argtypes = [vp, ctypes.c_int64, i32, vp, i32, vp]
+    lib.mla_peak_hbm_read.restype = i32
+    lib.mla_peak_mfma.argtypes = [i32, i32, vp, i32, vp]
+    lib.mla_peak_mfma.restype = i32
     return lib
 
 
@@ -340,3 +348,21 @@ def kv_dynamic_scale(x, scale=None):
         raise MLAError(2, "scale must be a float32 tensor on x's device")
     _check(lib.mla_kv_dynamic_scale(x.data_ptr(), x.numel(), scale.data_ptr(), _stream(x.device)))
     return scale
+
+
+def peak_hbm_read(buf, mode, sink, workgroups):
+    """One streaming read of the uint8 device tensor `buf` (mla_peak_hbm_read)
+    on the current stream; `sink` is a uint32 device tensor of >= workgroups."""
+    assert buf.is_cuda and buf.dtype == torch.uint8 and buf.is_contiguous()
+    assert sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= workgroups
+    lib = load()
+    _check(lib.mla_peak_hbm_read(buf.data_ptr(), buf.numel(), mode, sink.data_ptr(), workgroups,
+                                 _stream(buf.device)))
+
+
+def peak_mfma(kind, iters, sink, workgroups):
+    """One dense MFMA stream (mla_peak_mfma) on the current stream; `sink` is a
+    float32 device tensor of >= workgroups."""
+    assert sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= workgroups
+    lib = load()
+    _check(lib.mla_peak_mfma(kind, iters, sink.data_ptr(), workgroups, _stream(sink.device)))

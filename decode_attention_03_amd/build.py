@@ -27,9 +27,9 @@ DEBUG_BUILD_DIR = os.path.join(PKG, "_build_debug")
 DEBUG_LIB_PATH = os.path.join(PKG, "libmla_hip_debug.so")
 # sha256 of the gfx950 assembly of each kernel source, written by build()
 DEVICE_CODE_PATH = os.path.join(BUILD_DIR, "device_code.json")
-KERNEL_SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip"]
+KERNEL_SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip", "mla_peaks.hip"]
 
-SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip", "mla_api.cpp"]
+SOURCES = ["mla_split.hip", "mla_merge.hip", "mla_kv.hip", "mla_peaks.hip", "mla_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -42,6 +42,24 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_exports_every_peak_symbol(lib):
+    """include/mla_peaks.h (measured-peak microbenchmarks) is exported too, and
+    its host-side validation rejects bad arguments before any launch."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mla_peaks.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    assert set(names) == set(_lib.PEAK_EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.mla_peak_hbm_read(None, 1 << 20, 0, None, 64, None) == NULL
+    fake = ctypes.c_void_p(1 << 40)   # never dereferenced: rejected first
+    assert lib.mla_peak_hbm_read(fake, 1000, 0, fake, 64, None) == SHAPE
+    assert lib.mla_peak_hbm_read(fake, 1 << 20, 2, fake, 64, None) == SHAPE
+    assert lib.mla_peak_hbm_read(fake, 1 << 20, 0, fake, 0, None) == SHAPE
+    assert lib.mla_peak_mfma(0, 0, fake, 64, None) == SHAPE
+    assert lib.mla_peak_mfma(2, 10, fake, 64, None) == SHAPE
+    assert lib.mla_peak_mfma(0, 10, None, 64, None) == NULL
+
+
 def test_missing_library_fails_loudly(tmp_path):
     saved = _lib._LIB
     _lib._LIB = None
