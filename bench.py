@@ -208,6 +208,13 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
     mops8 = m.get("SQ_INSTS_VALU_MFMA_MOPS_F8", (0.0, 0))[0]
     mops16 = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", (0.0, 0))[0]
     busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", (0.0, 0))[0]
+    gui = m.get("GRBM_GUI_ACTIVE", (0.0, 0))[0]
+    lds_conf = m.get("SQ_LDS_BANK_CONFLICT", (0.0, 0))[0]
+    lds_act = m.get("SQ_LDS_IDX_ACTIVE", (0.0, 0))[0]
+    # MFMA busy: busy cycles per SIMD (the counter sums 1,024 SIMDs) over the
+    # cycles the GPU was active per XCD (the counter sums 8 XCDs)
+    mfma_busy_frac = (busy / 1024.0) / (gui / 8.0) if gui > 0 else None
+    lds_conf_frac = lds_conf / lds_act if lds_act > 0 else None
     mfma_flops = (mops8 + mops16) * 512.0
     rec = {
         "kernel": split_stat[0]["Name"],
@@ -231,7 +238,12 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
         "mfma": {"executed_flops_per_dispatch": mfma_flops,
                  "executed_tflops": round(mfma_flops / (split_avg_us * 1e-6) / 1e12, 2),
                  "mfma_busy_cycles_per_dispatch": busy,
+                 "grbm_gui_active_per_dispatch": gui,
+                 "mfma_busy_fraction": None if mfma_busy_frac is None else round(mfma_busy_frac, 4),
                  "counters": "SQ_INSTS_VALU_MFMA_MOPS_F8/BF16 x 512 flops"},
+        "lds": {"bank_conflict_cycles_per_dispatch": lds_conf,
+                "lds_active_cycles_per_dispatch": lds_act,
+                "bank_conflict_fraction": None if lds_conf_frac is None else round(lds_conf_frac, 4)},
         "commands": [_command_of(d) for d in (fetch_dir, write_dir, mfma_dir)],
     }
     json.dump(rec, open(os.path.join(PROFILES, f"split_traffic__{tag}.json"), "w"), indent=1)
@@ -257,7 +269,12 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
            f"| HBM bytes per merge dispatch (calibrated) | {merge_bytes / 1e6:.2f} MB |",
            f"| executed MFMA flops per split dispatch | {mfma_flops / 1e9:.2f} GFLOP "
            f"({mfma_flops / (split_avg_us * 1e-6) / 1e12:.1f} TFLOP/s) |",
-           f"| MFMA busy cycles per split dispatch (sum over SIMDs) | {busy:.3g} |"]
+           f"| MFMA busy cycles per split dispatch (sum over SIMDs) | {busy:.3g} |",
+           "| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over GRBM_GUI_ACTIVE / 8 XCDs) | "
+           + ("n/a" if mfma_busy_frac is None else f"{mfma_busy_frac * 100:.1f}%") + " |",
+           "| LDS bank-conflict cycles / LDS active cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE) | "
+           + ("n/a" if lds_conf_frac is None else f"{lds_conf:.3g} / {lds_act:.3g} = {lds_conf_frac * 100:.1f}%")
+           + " |"]
     open(os.path.join(PROFILES, f"split_traffic__{tag}.md"), "w").write("\n".join(md) + "\n")
     print("\n".join(md))
 
