@@ -64,6 +64,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -742,6 +744,24 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
+// Four bf16 query values (two dwords) q -> hi = RNE FP8 of q / isc and lo =
+// RNE FP8 of (q - hi * isc) / isc, packed 4 per dword (isc a power of two).
+// The scaled conversions divide by isc on the way to FP8 and multiply by it
+// on the way back, exactly, so hi and lo are those of q * 2^e with isc = 2^-e.
+__device__ __forceinline__ void split4_bf16_fp8(uint32_t d0, uint32_t d1, float isc, int& hi, int& lo) {
+  const s16x2 z = {0, 0};
+  s16x2 h = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(z, __builtin_bit_cast(bf16x2, d0), isc, false);
+  h = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(h, __builtin_bit_cast(bf16x2, d1), isc, true);
+  hi = __builtin_bit_cast(int, h);
+  const f32x2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, isc, false);
+  const f32x2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, isc, true);
+  s16x2 l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, __uint_as_float(d0 << 16) - b01[0],
+                                                     __uint_as_float(d0 & 0xFFFF0000u) - b01[1], isc, false);
+  l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, __uint_as_float(d1 << 16) - b23[0],
+                                               __uint_as_float(d1 & 0xFFFF0000u) - b23[1], isc, true);
+  lo = __builtin_bit_cast(int, l);
+}
+
 // four fp32 values -> (RNE FP8 of each, RNE FP8 of each residual), packed 4 per dword
 __device__ __forceinline__ void split4_fp8(float v0, float v1, float v2, float v3, int& hi, int& lo) {
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
@@ -1056,14 +1076,17 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       if (dh) read_q_f8<4>(qa, qv);
       else read_q_f8<5>(qa, qv);
     }
-    float mx = 0.f;
+    // largest magnitude of the lane's values: the magnitude bits of bf16
+    // values order as integers, two per dword (packed 16-bit maximum)
+    u16x2 mk = {0, 0};
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(qv[ks][c][k])), fabsf(bf16_hi(qv[ks][c][k]))));
+          mk = __builtin_elementwise_max(mk, __builtin_bit_cast(u16x2, qv[ks][c][k] & 0x7FFF7FFFu));
+    float mx = __uint_as_float((uint32_t)max(mk[0], mk[1]) << 16);
     mx = max32(mx);                                 // the two lanes holding this row
     if (h == 0) qmax[w][r32] = mx;
     lds_barrier();   // also: every wave has read the staged query
@@ -1077,7 +1100,6 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126;  // mx = m * 2^ex, m in [0.5, 1)
       e = min(max(7 - ex, -100), 100);
     }
-    const float sc = pow2f(e);
     q_unscale = pow2f(-e);
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks) {
@@ -1087,10 +1109,10 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       for (int c = 0; c < 4; ++c) {
         const u32x4 v = qv[ks][c];
         int hh, ll;
-        split4_fp8(bf16_lo(v[0]) * sc, bf16_hi(v[0]) * sc, bf16_lo(v[1]) * sc, bf16_hi(v[1]) * sc, hh, ll);
+        split4_bf16_fp8(v[0], v[1], q_unscale, hh, ll);
         hi8[2 * c] = hh;
         lo8[2 * c] = ll;
-        split4_fp8(bf16_lo(v[2]) * sc, bf16_hi(v[2]) * sc, bf16_lo(v[3]) * sc, bf16_hi(v[3]) * sc, hh, ll);
+        split4_bf16_fp8(v[2], v[3], q_unscale, hh, ll);
         hi8[2 * c + 1] = hh;
         lo8[2 * c + 1] = ll;
       }
