@@ -535,6 +535,38 @@ def test_head_padding(gpu_lib):
     compare(o12, l12, ro, rl, "H=12")
 
 
+@pytest.mark.parametrize("dt,nq,S", [("fp8", 3, 4), ("fp8", 3, 1), ("bf16", 3, 4)])
+@pytest.mark.parametrize("neg_scale", [False, True])
+def test_query_row_magnitudes(gpu_lib, dt, nq, S, neg_scale):
+    """Query rows of very different magnitudes in one row block.  The FP8
+    kernel takes each row's exponent from its largest |q| (compared on the
+    bf16 magnitude bits) and writes the row as two FP8 terms; the rows here
+    are scaled by 2^-110 (past the exponent clamp), 2^-40, 2^-8, 1 and 4, one
+    is all zero, one holds bf16 subnormals only, one has its largest values in
+    the rope dims, one is negative throughout and one mixes 2^-20 and 2^10
+    elements.  A negative softmax scale reverses the order of the scores.
+    Every row matches the oracle on both KV types."""
+    _say(f"query magnitudes {dt} Q={nq} S={S} negative scale={neg_scale}")
+    inp = make_inputs([300, 1100], nq, 12, dt, seed=31 + nq + S, device="cuda")
+    q = inp.q.float()
+    scales = [2.0 ** -110, 2.0 ** -40, 2.0 ** -8, 1.0, 4.0, 0.0]
+    for h, sc in enumerate(scales):
+        q[:, :, h] *= sc
+    q[:, :, 6] = torch.sign(q[:, :, 6]) * 2.0 ** -130 * (1 + torch.rand_like(q[:, :, 6]))
+    q[:, :, 7, 512:] *= 16.0
+    q[:, :, 8] = -q[:, :, 8].abs()
+    mix = torch.full_like(q[:, :, 9], 2.0 ** -20)
+    mix[..., ::37] = 2.0 ** 10 / 64
+    q[:, :, 9] = mix * torch.sign(q[:, :, 9])
+    inp.q = q.to(torch.bfloat16).contiguous()
+    assert (inp.q[:, :, 6] != 0).any() and (inp.q[:, :, 6].float().abs() < 2.0 ** -126).all()
+    if neg_scale:
+        inp.softmax_scale = -inp.softmax_scale
+    out, lse = run_verify(gpu_lib, inp, num_splits=S)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, f"{dt} S={S} neg={neg_scale}")
+
+
 def test_verify_equals_truncated_decodes(gpu_lib):
     """Speculative verify is lossless: token j of a Q = 3 verify equals a decode
     over the first L - 3 + j + 1 positions (within tolerance of the oracle)."""
