@@ -51,6 +51,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c5b", "c6"])
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--split-policy", default="auto", choices=["auto", "per-sequence", "by-length"],
+                    help="how the splits are spread over the sequences (auto: by length for "
+                         "workloads of unequal lengths, else per sequence)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -88,16 +91,19 @@ def _layers(cfg, device):
     return layers, c
 
 
-def _profile_record(tag, num_splits):
+def _profile_record(tag, num_splits, policy):
     """The committed counter summary of the split kernel for this workload, or
     None when it is missing or was taken on other split-kernel device code (the
-    gfx950 assembly of the current build) or another split count."""
+    gfx950 assembly of the current build), another split count or another
+    split policy."""
     path = os.path.join(PROFILES, f"split_traffic__{tag}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     dev = _split_device_sha256()
     if dev is None or rec.get("split_device_sha256") != dev or rec.get("num_splits") != num_splits:
+        return None
+    if rec.get("split_policy", "per-sequence") != policy:
         return None
     return rec
 
@@ -221,6 +227,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
         "workload": tag,
         "config_key": cfg,
         "num_splits": S,
+        "split_policy": _recorded_config(trace_dir).get("split_policy", "per-sequence"),
         "split_device_sha256": _split_device_sha256(),
         "split_avg_us": round(split_avg_us, 3),
         "merge_avg_us": round(float(merge_stat[0]["AverageNs"]) / 1e3, 3) if merge_stat else None,
@@ -255,7 +262,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
            f"<mfma> --profile-tag {tag}`.", "",
            "| quantity | value |", "|---|---|",
            f"| split kernel average duration (kernel trace) | {split_avg_us:.2f} us |",
-           f"| split count | {S} |",
+           f"| split count | {S} ({rec['split_policy']} plan) |",
            f"| FETCH_SIZE per dispatch | {spl_f[0]:.0f} KiB |",
            f"| WRITE_SIZE per dispatch | {spl_w[0]:.0f} KiB |",
            f"| calibration: 1 GiB negation reads / writes | {cal_f[0]:.0f} / {cal_w[0]:.0f} KiB "
@@ -293,15 +300,21 @@ def config_tag(cfg):
     return {v: k for k, v in TAGS.items()}[cfg]
 
 
-def _recorded_splits(folder):
-    """Split count from the bench JSON line saved beside the trace (bench.json)."""
+def _recorded_config(folder):
+    """The config object of the bench JSON line saved beside the trace (bench.json)."""
     p = os.path.join(folder, "bench.json")
     if not os.path.exists(p):
-        return None
+        return {}
     for ln in open(p):
         if ln.startswith('{"metric"'):
-            return int(json.loads(ln)["config"]["num_splits"])
-    return None
+            return json.loads(ln)["config"]
+    return {}
+
+
+def _recorded_splits(folder):
+    """Split count from the bench JSON line saved beside the trace (bench.json)."""
+    n = _recorded_config(folder).get("num_splits")
+    return None if n is None else int(n)
 
 
 def _cpu_model():
@@ -510,6 +523,14 @@ def main():
     hint = cfg["seq_hi"]
     first = layers[0]
     S = mla.num_splits(first.q, first.kv, first.page_table, args.num_splits, hint)
+    ragged = cfg["seq_lo"] != cfg["seq_hi"]
+    policy_name = args.split_policy
+    if policy_name == "auto":
+        policy_name = "by-length" if ragged else "per-sequence"
+    policy = mla.SPLIT_BY_LENGTH if policy_name == "by-length" else mla.SPLIT_PER_SEQUENCE
+    # the split and merge of the plan by length run only inside mla_verify:
+    # the kernel legs below are timed together, as the layer-step
+    joint = policy == mla.SPLIT_BY_LENGTH and S > 1
 
     outs = [torch.empty((l.batch, l.num_q, l.heads, 512), dtype=torch.bfloat16, device=dev)
             for l in layers]
@@ -522,7 +543,8 @@ def main():
     def step():
         for i, l in enumerate(layers):
             mla.verify(l.q, l.kv, l.page_table, l.seq_lens, l.softmax_scale, l.kv_scale,
-                       num_splits=args.num_splits, max_seq_len_hint=hint, out=outs[i],
+                       num_splits=args.num_splits, max_seq_len_hint=hint, split_policy=policy,
+                       out=outs[i],
                        lse=lses[i], workspace=ws)
 
     # Same kernels, same launch configuration as mla_verify (split kernel, then
@@ -568,8 +590,10 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     graphs = {}
-    for name, fn in (("step", repeat(step)), ("split", repeat(split_only)),
-                     ("merge", repeat(merge_only))):
+    kinds = [("step", repeat(step))]
+    if not joint:
+        kinds += [("split", repeat(split_only)), ("merge", repeat(merge_only))]
+    for name, fn in kinds:
         stream.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(stream):
             fn()  # warm the capture stream
@@ -618,11 +642,11 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) / (n * reps) / n_layers * 1e3  # us per kernel launch
 
-    split_us = timed(graphs["split"], n_replays)
-    merge_us = timed(graphs["merge"], n_replays) if S > 1 else 0.0
+    split_us = timed(graphs["step" if joint else "split"], n_replays)
+    merge_us = timed(graphs["merge"], n_replays) if (S > 1 and not joint) else 0.0
     split_alg = float(np.mean(alg))     # one split launch processes one layer's batch
     achieved = split_alg / (split_us * 1e-6) / 1e9
-    prof = _profile_record(config_tag(args.config), S)
+    prof = _profile_record(config_tag(args.config), S, policy_name)
     traffic = None if prof is None else float(prof["hbm_bytes_per_dispatch"])
     # executed MFMA work of the split kernel (padded rows, two-term fp8 operands)
     fp8 = first.kv_dtype == "fp8"
@@ -639,14 +663,16 @@ def main():
     intensity = sum(flops) / bytes_per_step
     mfma_bound = intensity > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     split_flops = float(np.mean(flops))
+    kname = ("split_kernel + merge_kernel (plan by length: timed together, as the layer-step)"
+             if joint else "split_kernel")
     if mfma_bound:
         a_tf = split_flops / (split_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": "split_kernel", "achieved": round(a_tf, 2),
+        roofline = {"bound": "mfma", "kernel": kname, "achieved": round(a_tf, 2),
                     "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(a_tf / mfma_peak, 4),
                     "traffic": None if traffic is None else round(traffic),
                     "intensity_flop_per_byte": round(intensity, 1)}
     else:
-        roofline = {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 2),
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": None if traffic is None else round(traffic),
                     "intensity_flop_per_byte": round(intensity, 1)}
@@ -689,11 +715,13 @@ def main():
             "mfma_operands": ("fp8 e4m3 (q and p each split into two fp8 terms), fp32 accumulate"
                               if terms == 2 else "bf16, fp32 accumulate"),
             "num_splits": S,
+            "split_policy": policy_name,
             "algorithmic_bytes_per_step": int(bytes_per_step),
             "algorithmic_flops_per_step": int(sum(flops)),
             "mfma_tflops_algorithmic": round(sum(flops) / (ms_per_step * 1e-3) / 1e12, 2),
-            "split_kernel_us": round(split_us, 3),
-            "merge_kernel_us": round(merge_us, 3),
+            "split_kernel_us": None if joint else round(split_us, 3),
+            "merge_kernel_us": None if joint else round(merge_us, 3),
+            "split_and_merge_us": round(split_us, 3) if joint else None,
             "timing": (f"{timing_mode} (faster of: HIP graph of {reps} step(s) "
                        f"({reps * n_layers} layer calls) replayed, {graph_ms:.4f} ms; eager "
                        f"issue of one call per layer, {eager_ms:.4f} ms); per-kernel times "
@@ -704,7 +732,7 @@ def main():
         },
         "roofline": roofline,
         "mfma_roofline": {
-            "kernel": "split_kernel",
+            "kernel": kname,
             "executed_tflops": round(mfma_exec / (split_us * 1e-6) / 1e12, 2),
             "peak": mfma_peak,
             "unit": "TFLOP/s",
@@ -713,7 +741,10 @@ def main():
                     "2 x (576 + 512) flops per position",
         },
     }
-    _log(f"split {split_us:.2f} us, merge {merge_us:.2f} us per launch")
+    if joint:
+        _log(f"split + merge (plan by length) {split_us:.2f} us per layer")
+    else:
+        _log(f"split {split_us:.2f} us, merge {merge_us:.2f} us per launch")
     line["config"]["kv_append"] = _append_leg(mla, first, dev, args.warmup, args.steps)
     if first.heads > 12 and first.heads % 12 == 0:
         line["config"]["rank_merge"] = _rank_merge(mla, first, dev, args.warmup, args.steps)

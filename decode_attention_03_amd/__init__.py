@@ -10,6 +10,8 @@ from ._lib import (
     MLAError,
     MLA_KV_BF16,
     MLA_KV_FP8_E4M3,
+    SPLIT_BY_LENGTH,
+    SPLIT_PER_SEQUENCE,
     Params,
     decode,
     kv_append,
@@ -27,7 +29,8 @@ from ._lib import (
 from .build import LIB_PATH
 
 __all__ = [
-    "EXPORTS", "MLAError", "MLA_KV_BF16", "MLA_KV_FP8_E4M3", "Params", "decode", "kv_append",
+    "EXPORTS", "MLAError", "MLA_KV_BF16", "MLA_KV_FP8_E4M3", "SPLIT_BY_LENGTH",
+    "SPLIT_PER_SEQUENCE", "Params", "decode", "kv_append",
     "kv_dynamic_scale", "load",
     "make_params", "merge", "num_splits", "split", "verify", "verify_static", "workspace_size",
     "STATIC_SCRATCH_BYTES", "LIB_PATH",

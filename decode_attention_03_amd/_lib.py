@@ -15,6 +15,9 @@ from .build import DEBUG_LIB_PATH, LIB_PATH
 
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
+# mla_split_policy
+SPLIT_PER_SEQUENCE = 0
+SPLIT_BY_LENGTH = 1
 LATENT_DIM = 576
 VALUE_DIM = 512
 
@@ -53,6 +56,7 @@ class Params(ctypes.Structure):
         ("max_seq_len_hint", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
+        ("split_policy", ctypes.c_int32),
     ]
 
 
@@ -145,11 +149,12 @@ def _kv_dtype(kv_cache):
     raise MLAError(3, f"kv_cache dtype {kv_cache.dtype} is neither bfloat16 nor FP8 E4M3FN bytes")
 
 
-def make_params(q, kv_cache, page_table, num_splits=0, max_seq_len_hint=0):
+def make_params(q, kv_cache, page_table, num_splits=0, max_seq_len_hint=0,
+                split_policy=SPLIT_PER_SEQUENCE):
     return Params(batch=q.shape[0], num_q_tokens=q.shape[1], num_heads=q.shape[2],
                   num_blocks=kv_cache.shape[0], max_blocks_per_seq=page_table.shape[1],
                   max_seq_len_hint=int(max_seq_len_hint), kv_dtype=_kv_dtype(kv_cache),
-                  num_splits=int(num_splits))
+                  num_splits=int(num_splits), split_policy=int(split_policy))
 
 
 def _check_inputs(q, kv_cache, page_table, seq_lens):
@@ -193,10 +198,10 @@ def workspace_size(q, kv_cache, page_table, num_splits=0, max_seq_len_hint=0):
 
 
 def _attend(entry, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, num_splits,
-            max_seq_len_hint, out, lse, workspace):
+            max_seq_len_hint, out, lse, workspace, split_policy):
     lib = load()
     _check_inputs(q, kv_cache, page_table, seq_lens)
-    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
+    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint, split_policy)
     B, Q, H, _ = q.shape
     if out is None:
         out = torch.empty((B, Q, H, VALUE_DIM), dtype=torch.bfloat16, device=q.device)
@@ -219,27 +224,29 @@ def _attend(entry, q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale, n
 
 
 def decode(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
-           max_seq_len_hint=0, out=None, lse=None, workspace=None):
+           max_seq_len_hint=0, out=None, lse=None, workspace=None,
+           split_policy=SPLIT_PER_SEQUENCE):
     """mla_decode: Q = 1.  Returns (out bf16 [B,1,H,512], lse fp32 [B,1,H])."""
     return _attend("mla_decode", q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale,
-                   num_splits, max_seq_len_hint, out, lse, workspace)
+                   num_splits, max_seq_len_hint, out, lse, workspace, split_policy)
 
 
 def verify(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
-           max_seq_len_hint=0, out=None, lse=None, workspace=None):
+           max_seq_len_hint=0, out=None, lse=None, workspace=None,
+           split_policy=SPLIT_PER_SEQUENCE):
     """mla_verify: Q query tokens with the causal rule.  Returns (out, lse)."""
     return _attend("mla_verify", q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale,
-                   num_splits, max_seq_len_hint, out, lse, workspace)
+                   num_splits, max_seq_len_hint, out, lse, workspace, split_policy)
 
 
 def verify_static(q, kv_cache, page_table, seq_lens, softmax_scale, kv_scale=1.0, num_splits=0,
-                  max_seq_len_hint=0, out=None, lse=None):
+                  max_seq_len_hint=0, out=None, lse=None, split_policy=SPLIT_PER_SEQUENCE):
     """mla_verify_static: as verify, with the split partials in the library's static
     per-GPU array instead of a workspace (the C call allocates nothing).  Calls
     that overlap in time on one GPU race on that array."""
     lib = load()
     _check_inputs(q, kv_cache, page_table, seq_lens)
-    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint)
+    p = make_params(q, kv_cache, page_table, num_splits, max_seq_len_hint, split_policy)
     B, Q, H, _ = q.shape
     if out is None:
         out = torch.empty((B, Q, H, VALUE_DIM), dtype=torch.bfloat16, device=q.device)

@@ -49,7 +49,19 @@ mla_status check_params(const mla_params* p, int max_q) {
   if (p->max_seq_len_hint < 0) return MLA_ERR_BAD_SHAPE;
   if (p->num_splits < 0 || p->num_splits > mla::kMaxSplits) return MLA_ERR_BAD_SHAPE;
   if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_BAD_DTYPE;
+  if (p->split_policy != MLA_SPLIT_PER_SEQUENCE && p->split_policy != MLA_SPLIT_BY_LENGTH)
+    return MLA_ERR_BAD_SHAPE;
   return MLA_OK;
+}
+
+// Whether a call with S splits uses the plan by length (see include/mla.h):
+// the kernels compute it with one wave (a batch of at most 64), and the
+// merge keeps a weight table of up to S * B - B + 1 floats per row in LDS.
+constexpr int64_t kMaxByLengthSlots = 12288;
+bool uses_by_length(const mla_params* p, int32_t S) {
+  const int64_t B = p->batch;
+  return p->split_policy == MLA_SPLIT_BY_LENGTH && B >= 2 && B <= mla::kMaxBatchByLength && S > 1 &&
+         (int64_t)S * B - B + 1 <= kMaxByLengthSlots;
 }
 
 int32_t choose_splits(const mla_params* p) {
@@ -123,6 +135,7 @@ bool launches_fit(const mla::SplitArgs& a, const mla_params* p, int32_t S) {
   mla::MergeArgs m{};
   m.rows = (int64_t)rows_of(p);
   m.num_splits = S;
+  m.by_length = a.by_length;
   return mla::merge_work_items(m) <= mla::kMaxWorkItems;
 }
 
@@ -212,6 +225,7 @@ mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
   const int32_t S = choose_splits(p);
   hipStream_t s = (hipStream_t)stream;
   mla::SplitArgs a = make_args(p, q, kv, pt, sl, softmax_scale, kv_scale, S);
+  a.by_length = uses_by_length(p, S) ? 1 : 0;
   if (!launches_fit(a, p, S)) return MLA_ERR_UNSUPPORTED;
   st = debug_flags_ptr(s, &a.debug_flags);
   if (st != MLA_OK) return st;
@@ -240,6 +254,11 @@ mla_status attend(const mla_params* p, int max_q, const void* q, const void* kv,
   m.lse = lse;
   m.rows = (int64_t)rows_of(p);
   m.num_splits = S;
+  m.by_length = a.by_length;
+  m.batch = p->batch;
+  m.rows_per_seq = p->num_q_tokens * p->num_heads;
+  m.max_blocks = p->max_blocks_per_seq;
+  m.seq_lens = sl;
   return hip_status(mla::launch_merge(m, s));
 }
 
@@ -286,6 +305,7 @@ mla_status mla_split(const mla_params* p, const void* q, const void* kv_cache,
                      float kv_scale, void* part_out, float* part_lse, void* stream) {
   mla_status st = check_params(p, mla::kMaxQ);
   if (st != MLA_OK) return st;
+  if (p->split_policy != MLA_SPLIT_PER_SEQUENCE) return MLA_ERR_UNSUPPORTED;   // partials per sequence
   if (!q || !kv_cache || !page_table || !seq_lens || !part_out || !part_lse) return MLA_ERR_NULL_ARG;
   st = check_scales(softmax_scale, kv_scale, p->kv_dtype);
   if (st != MLA_OK) return st;

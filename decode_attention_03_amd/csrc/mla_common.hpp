@@ -44,16 +44,68 @@ struct SplitArgs {
   float out_scale;            // kv_scale (value vectors are used undecoded-scale in the MFMA)
   int32_t num_blocks;         // pool blocks (checked by the debug build only)
   uint32_t* debug_flags;      // debug build: contract violations found (kDbg* bits)
+  int32_t by_length;          // split plan by length (balanced_plan), else S per sequence
 };
 
 struct MergeArgs {
-  const uint16_t* part_out;   // bf16 [S][rows][512]
-  const float* part_lse;      // [S][rows]
+  const uint16_t* part_out;   // bf16 [S][rows][512], or [S * batch slots][R][512] by length
+  const float* part_lse;      // [S][rows], or [S * batch slots][R]
   uint16_t* out;              // bf16 [rows][512]
   float* lse;                 // [rows]
   int64_t rows;
   int32_t num_splits;
+  // split plan by length: the partials of row b * R + r are the slots of
+  // sequence b (balanced_plan over seq_lens), R = rows per sequence
+  int32_t by_length;
+  int32_t batch;
+  int32_t rows_per_seq;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
 };
+
+// Split plan by length.  The G = S * B split slots of a launch are shared
+// among the B sequences in proportion to their pages, at least one each:
+// sequence b owns slots [C(b - 1), C(b)) with
+//   C(b) = b + 1 + floor((G - B) * (P_0 + ... + P_b) / (P_0 + ... + P_{B-1})),
+// C(-1) = 0, P_i = ceil(seq_lens[i] / 16) clamped into [1, max_blocks], so a
+// long sequence gets many splits and a short one few, and every split slot
+// covers about the same number of pages.  Computed by one wave (B <= 64, one
+// sequence per lane: a lane-prefix sum and a ballot); every workgroup of the
+// split and merge launches computes the same plan from seq_lens.  Returns,
+// for the sequence found by `find` (a slot w when by_slot, else a sequence
+// index), its first slot and slot count.
+constexpr int kMaxBatchByLength = 64;
+
+struct SeqSlots {
+  int b, first, count;
+};
+__device__ __forceinline__ SeqSlots balanced_plan(const int32_t* seq_lens, int B, int S, int max_blocks,
+                                                  int find, bool by_slot) {
+  const int lane = (int)(threadIdx.x & 63);
+  int P = 0;
+  if (lane < B) P = min(max((seq_lens[lane] + kPage - 1) / kPage, 1), max(max_blocks, 1));
+  int pref = P;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(pref, d);
+    if (lane >= d) pref += t;
+  }
+  const int ptot = __shfl(pref, 63);
+  const int G = S * B;
+  int C = G + 1;   // lanes past the batch: past every slot
+  if (lane < B) C = lane + 1 + (int)(((int64_t)(G - B) * pref) / max(ptot, 1));
+  int b;
+  if (by_slot) b = __builtin_ctzll(__ballot(C > find));
+  else b = find;
+  b = __builtin_amdgcn_readfirstlane(b);
+  const int hi = __shfl(C, b);
+  const int lo = __shfl(C, max(b - 1, 0));
+  SeqSlots r;
+  r.b = b;
+  r.first = __builtin_amdgcn_readfirstlane(b > 0 ? lo : 0);
+  r.count = __builtin_amdgcn_readfirstlane(hi) - r.first;
+  return r;
+}
 
 struct AppendArgs {
   const uint16_t* kv_new;     // bf16 [B][Q][576]

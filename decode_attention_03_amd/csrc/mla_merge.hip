@@ -66,25 +66,39 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int tid = threadIdx.x;
   const int rs = tid / kTPR;
   const int t = tid % kTPR;
-  const int S = a.num_splits;
   const int64_t row = ((int64_t)blockIdx.x / kSlices) * kRPW + rs;
   const int slice = (int)(blockIdx.x % kSlices);
   const bool live = row < a.rows;
-  float* cf = coef + rs * S;
+  const int64_t lrow = live ? row : 0;
+  // the row's partials: S of them, partial s at row pbase + s * pstride of
+  // part_out / part_lse (with the plan by length, the slots of the row's
+  // sequence; every wave of a row slice computes the plan for that sequence)
+  int S = a.num_splits;
+  int64_t pbase = lrow, pstride = a.rows;
+  int cstride = a.num_splits;   // floats of coef per row slice
+  if (a.by_length) {
+    const int R = a.rows_per_seq;
+    const int bq = (int)(lrow / R);
+    const SeqSlots ss = balanced_plan(a.seq_lens, a.batch, a.num_splits, a.max_blocks, bq, false);
+    S = ss.count;
+    pbase = (int64_t)ss.first * R + (lrow - (int64_t)bq * R);
+    pstride = R;
+    cstride = a.num_splits * a.batch - a.batch + 1;   // the most slots one sequence can own
+  }
+  float* cf = coef + rs * cstride;
 
   const int chunk = t % kChunks;
   const int lane_s = t / kChunks;
   const int col = slice * COLS + 4 * chunk;
-  const uint16_t* const po = a.part_out + (live ? row : (int64_t)0) * kValue + col;
-  const int64_t stride = a.rows * kValue;
+  const uint16_t* const po = a.part_out + pbase * kValue + col;
+  const int64_t stride = pstride * kValue;
   // lse of split t (the first of this thread's), kept for the weights; issued
   // first, so that waiting for it leaves the partial loads below in flight
   // (loads retire from the wait counter in issue order)
-  const int64_t lrow = live ? row : 0;
-  const float ls_t = a.part_lse[(int64_t)min(t, S - 1) * a.rows + lrow];
+  const float ls_t = a.part_lse[pbase + (int64_t)min(t, S - 1) * pstride];
   // first round of partial loads (splits lane_s + LANES u), in flight during
   // the lse reductions.  The loads are unconditional (split index clamped to
-  // S - 1, row 0 for a dead slice: the buffer holds all S x rows partials), so
+  // S - 1, row 0 for a dead slice: the buffer holds all of those partials), so
   // no branch with its own wait sits between them; a split past S, like an
   // empty one, has weight zero below and its value is not used.
   u32x2 v[kInFlight];   // four bf16 each
@@ -96,13 +110,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const float ls0 = (live && t < S) ? ls_t : kNegInf;
   float m = ls0;
   if (live)
-    for (int s = t + kTPR; s < S; s += kTPR) m = fmaxf(m, a.part_lse[(int64_t)s * a.rows + row]);
+    for (int s = t + kTPR; s < S; s += kTPR) m = fmaxf(m, a.part_lse[pbase + (int64_t)s * pstride]);
   m = slice_reduce<kWPR, true>(m, red);
 
   float wsum = 0.f;
   if (live)
     for (int s = t; s < S; s += kTPR) {
-      const float ls = s == t ? ls0 : a.part_lse[(int64_t)s * a.rows + row];
+      const float ls = s == t ? ls0 : a.part_lse[pbase + (int64_t)s * pstride];
       const float wgt = (ls == kNegInf) ? 0.f : expf(ls - m);
       cf[s] = wgt;
       wsum += wgt;
@@ -148,11 +162,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   }
 }
 
+// Shape by the split count of a row.  With the plan by length the rows of the
+// longest sequences, which set the time, hold about twice the average: up to
+// 16 on average that moves the shape to two lanes per chunk (c2, 8 splits:
+// 5.7 -> 5.1 us); at 32 the whole-row shape stays the faster one (c3: 11.9 us
+// against 14.2 for quarter rows).
+int shape_splits(const MergeArgs& a) {
+  return (a.by_length && a.num_splits <= 16) ? 2 * a.num_splits : a.num_splits;
+}
+
 template <int LANES, int COLS>
 hipError_t launch_shape(const MergeArgs& a, hipStream_t stream) {
   constexpr int kRPW = kMergeThreads / (LANES * COLS / 4);
   const int64_t groups = (a.rows + kRPW - 1) / kRPW;
-  const size_t lds = (size_t)kRPW * a.num_splits * sizeof(float);
+  const int cstride = a.by_length ? a.num_splits * a.batch - a.batch + 1 : a.num_splits;
+  const size_t lds = (size_t)kRPW * cstride * sizeof(float);
   hipLaunchKernelGGL((merge_kernel<LANES, COLS>), dim3((unsigned)(groups * (kValue / COLS))),
                      dim3(kMergeThreads), lds, stream, a);
   return hipGetLastError();
@@ -162,14 +186,16 @@ hipError_t launch_shape(const MergeArgs& a, hipStream_t stream) {
 
 int64_t merge_work_items(const MergeArgs& a) {
   // the grids of launch_shape for the shapes launch_merge picks
-  if (a.num_splits <= 8) return (a.rows + 1) / 2 * kMergeThreads;   // two rows per workgroup
-  if (a.num_splits <= 32) return a.rows * kMergeThreads;            // one row per workgroup
-  return a.rows * 4 * kMergeThreads;                                // four quarters per row
+  const int s = shape_splits(a);
+  if (s <= 8) return (a.rows + 1) / 2 * kMergeThreads;   // two rows per workgroup
+  if (s <= 32) return a.rows * kMergeThreads;            // one row per workgroup
+  return a.rows * 4 * kMergeThreads;                     // four quarters per row
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  if (a.num_splits <= 8) return launch_shape<1, 512>(a, stream);
-  if (a.num_splits <= 32) return launch_shape<2, 512>(a, stream);
+  const int s = shape_splits(a);
+  if (s <= 8) return launch_shape<1, 512>(a, stream);
+  if (s <= 32) return launch_shape<2, 512>(a, stream);
   return launch_shape<8, 128>(a, stream);
 }
 

@@ -90,6 +90,8 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 // else the row block is simply the slowest index.
 struct WgCoord {
   int split, b, z;
+  int nsplit;     // splits of sequence b
+  int64_t slot;   // partial slot: rows slot * R .. of part_out / part_lse
 };
 __device__ __forceinline__ WgCoord wg_coord(int num_splits, int batch, int row_blocks) {
   const int id = (int)blockIdx.x;
@@ -107,6 +109,26 @@ __device__ __forceinline__ WgCoord wg_coord(int num_splits, int batch, int row_b
   c.split = u % num_splits;
   c.b = u / num_splits;
   c.z = z;
+  c.nsplit = num_splits;
+  c.slot = 0;
+  return c;
+}
+
+// The workgroup's split: with S splits per sequence, unit u = split + S b of
+// wg_coord and slot split * B + b; with the plan by length, unit u is slot u,
+// which balanced_plan maps to its sequence and its index among that
+// sequence's splits.
+__device__ __forceinline__ WgCoord split_coord(const SplitArgs& a, int row_blocks) {
+  WgCoord c = wg_coord(a.num_splits, a.batch, row_blocks);
+  c.slot = (int64_t)c.split * a.batch + c.b;
+  if (a.by_length) {
+    const int u = c.split + a.num_splits * c.b;
+    const SeqSlots ss = balanced_plan(a.seq_lens, a.batch, a.num_splits, a.max_blocks, u, true);
+    c.b = ss.b;
+    c.split = u - ss.first;
+    c.nsplit = ss.count;
+    c.slot = u;
+  }
   return c;
 }
 
@@ -318,14 +340,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const bool t32 = !L16 && w < 2;  // layout 48: wave works on the 32-row tile
   const int H = a.heads;
   const int R = a.num_q * H;
-  const WgCoord wc = wg_coord(a.num_splits, a.batch, (R + RPAD - 1) / RPAD);
+  const WgCoord wc = split_coord(a, (R + RPAD - 1) / RPAD);
   const int split = wc.split;
   const int b = wc.b;
 
   const int L = kDebug ? debug_seq_len(a.seq_lens[b], a.num_q, a.max_blocks, a.debug_flags) : a.seq_lens[b];
   const int P = (L + kPage - 1) / kPage;
-  const int p0 = (int)(((int64_t)split * P) / a.num_splits);
-  const int p1 = (int)(((int64_t)(split + 1) * P) / a.num_splits);
+  const int p0 = (int)(((int64_t)split * P) / wc.nsplit);
+  const int p1 = (int)(((int64_t)(split + 1) * P) / wc.nsplit);
   const int ntiles = (p1 - p0 + TPG - 1) / TPG;
   // read-only page table through the constant address space: uniform
   // indices become scalar loads, which do not count against vmcnt
@@ -685,7 +707,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     }
     // each wave reads back only its own rows (LDS is in order within a wave)
     uint16_t* const dst = FINAL ? a.out : a.part_out;
-    const int64_t row0 = FINAL ? (int64_t)b * R : ((int64_t)split * a.batch + b) * R;
+    const int64_t row0 = FINAL ? (int64_t)b * R : wc.slot * R;
     const int cc = 8 * (lane & 15);
 #pragma unroll
     for (int j = 0; j < RPAD / 4; ++j) {
@@ -696,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   }
   auto store_lse = [&](int r, float m_run, float l_run) {
     const float v = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
-    const int64_t lrow = ((FINAL ? 0 : (int64_t)split * a.batch) + b) * R + rb0 + r;
+    const int64_t lrow = (FINAL ? (int64_t)b : wc.slot) * R + rb0 + r;
     if constexpr (FINAL) a.lse[lrow] = v;
     else a.part_lse[lrow] = v;
   };
@@ -940,7 +962,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int ks0 = dh ? 5 : 0;
   const int H = a.heads;
   const int R = a.num_q * H;
-  const WgCoord wc = wg_coord(a.num_splits, a.batch, (R + 63) / 64);
+  const WgCoord wc = split_coord(a, (R + 63) / 64);
   const int split = wc.split;
   const int b = wc.b;
   // rows 64 * wc.z .. + 63 of the Q*H query rows are this workgroup's
@@ -966,7 +988,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int P = (L + kPage - 1) / kPage;
   // page range [floor(split P / S), floor((split + 1) P / S)) in 32-bit
   // arithmetic: floor(s P / S) = s floor(P / S) + floor(s (P mod S) / S)
-  const int S = a.num_splits;
+  const int S = wc.nsplit;
   const int pq = P / S, pr = P - pq * S;
   const int p0 = split * pq + (split * pr) / S;
   const int p1 = (split + 1) * pq + ((split + 1) * pr) / S;
@@ -1486,7 +1508,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       }
     // each wave reads back only its own rows (LDS is in order within a wave)
     uint16_t* const dst = FINAL ? a.out : a.part_out;
-    const int64_t row0 = FINAL ? (int64_t)b * R : ((int64_t)split * a.batch + b) * R;
+    const int64_t row0 = FINAL ? (int64_t)b * R : wc.slot * R;
     const int cc = 8 * (lane & 15);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -1499,7 +1521,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   if (myrow < R && v4 == 0 && h == 0) {
     const float lv = (l_run > 0.f) ? (mref + log2f(l_run)) * kLn2 : kNegInf;
     if constexpr (FINAL) a.lse[(int64_t)b * R + myrow] = lv;
-    else a.part_lse[((int64_t)split * a.batch + b) * R + myrow] = lv;
+    else a.part_lse[wc.slot * R + myrow] = lv;
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }

@@ -117,7 +117,30 @@ typedef struct {
                                  Only steers the automatic split count. */
   int32_t kv_dtype;           /* mla_kv_dtype */
   int32_t num_splits;         /* 0 = library chooses; 1..256 = exactly this many splits */
+  int32_t split_policy;       /* mla_split_policy: how the S * batch split slots are spread */
 } mla_params;
+
+/* How mla_decode / mla_verify / mla_verify_static spread the S * batch split
+ * slots of a call (S = mla_num_splits) over the sequences.  Results are the
+ * same up to rounding order either way; only the work per workgroup differs.
+ *   MLA_SPLIT_PER_SEQUENCE: every sequence gets S splits (S is chosen from the
+ *     longest expected sequence), so with unequal lengths the splits of long
+ *     sequences hold many more pages than those of short ones;
+ *   MLA_SPLIT_BY_LENGTH: sequence b gets C(b) - C(b - 1) slots with
+ *     C(b) = b + 1 + floor((S*B - B) * (P_0 + ... + P_b) / (P_0 + ... + P_{B-1})),
+ *     P_i = ceil(seq_lens[i] / 16) clamped into [1, max_blocks_per_seq] --
+ *     at least one each, the rest in proportion to its pages -- so every
+ *     workgroup gets about the same number of pages (the history "divided into
+ *     pieces processed by parallel workgroups", "Inside Kimi K3 optimization",
+ *     section "4. MLA").  The kernels compute the plan on the device from
+ *     seq_lens.  Used for 2 <= batch <= 64 and S > 1 when the merge's weight
+ *     table fits (S * batch - batch + 1 <= 12,288); otherwise the call uses
+ *     MLA_SPLIT_PER_SEQUENCE.  mla_split, whose partial layout is per
+ *     sequence, returns MLA_ERR_UNSUPPORTED for it. */
+typedef enum {
+  MLA_SPLIT_PER_SEQUENCE = 0,
+  MLA_SPLIT_BY_LENGTH = 1
+} mla_split_policy;
 
 /* Split count the library uses for these parameters (>= 1), or 0 if the
  * parameters are invalid.  Depends only on host-side values: with num_splits

@@ -179,6 +179,21 @@ def test_grid_size_limit(lib):
     assert lib.mla_merge(FAKE, FAKE, 64, 1 << 22, FAKE, FAKE, None) == UNSUPPORTED
 
 
+def test_split_policy_validation(lib):
+    """split_policy is MLA_SPLIT_PER_SEQUENCE (0) or MLA_SPLIT_BY_LENGTH (1);
+    mla_split keeps its per-sequence partial layout and refuses the other."""
+    assert _verify(lib, params(split_policy=2)) == SHAPE
+    assert _verify(lib, params(split_policy=-1)) == SHAPE
+    assert _verify(lib, params(split_policy=1, num_splits=4)) == WS     # valid: reaches the workspace check
+    assert lib.mla_split(ctypes.byref(params(split_policy=1)), FAKE, FAKE, FAKE, FAKE, 0.07, 0.03,
+                         FAKE, FAKE, None) == UNSUPPORTED
+    # the split count and workspace do not depend on the policy
+    for kw in (dict(), dict(batch=64, max_seq_len_hint=65536), dict(batch=32, kv_dtype=0)):
+        a, b = params(**kw), params(split_policy=1, **kw)
+        assert lib.mla_num_splits(ctypes.byref(a)) == lib.mla_num_splits(ctypes.byref(b))
+        assert lib.mla_workspace_size(ctypes.byref(a)) == lib.mla_workspace_size(ctypes.byref(b))
+
+
 def test_decode_rejects_multi_token(lib):
     assert _verify(lib, params(num_q_tokens=2), entry="mla_decode") == SHAPE
 

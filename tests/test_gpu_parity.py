@@ -449,6 +449,76 @@ def test_graph_replay_matches_eager(gpu_lib, dt, nq, S):
         assert torch.equal(out, out_e) and torch.equal(lse, lse_e), f"replay {i}"
 
 
+# The split plan by length (MLA_SPLIT_BY_LENGTH): the S * B split slots spread
+# over the sequences in proportion to their pages.  Very unequal lengths,
+# sequences shorter than a page, both kernels, several row blocks, the
+# largest batch the plan takes (64) and one past it (per-sequence plan used).
+BY_LENGTH_CASES = [
+    # (seq_lens, Q, H, kv_dtype, num_splits)
+    ([16, 40000, 33, 5000], 3, 12, "fp8", 0),
+    ([16, 40000, 33, 5000], 3, 12, "fp8", 64),
+    ([1, 15, 16, 17, 64, 65, 200, 3000], 1, 12, "bf16", 0),
+    ([3, 300, 1029, 7000], 3, 96, "fp8", 4),
+    ([100, 8000], 8, 12, "bf16", 6),
+    ([5, 9000, 700], 3, 12, "bf16", 9),
+    ([2000, 30], 1, 12, "fp8", 16),
+]
+
+
+@pytest.mark.parametrize("case", BY_LENGTH_CASES, ids=[f"{c[3]}-Q{c[1]}-H{c[2]}-S{c[4]}-{len(c[0])}seq"
+                                                       for c in BY_LENGTH_CASES])
+def test_split_by_length(gpu_lib, case):
+    """The plan by length gives the oracle's result (with NaN-poisoned spare
+    blocks and page tails), within tolerance of the per-sequence plan."""
+    lens, nq, nh, dt, S = case
+    _say(f"split by length {case}")
+    inp = make_inputs(lens, nq, nh, dt, seed=11 * sum(lens) + nq + nh, device="cuda",
+                      spare_blocks=2, poison=True)
+    out, lse = run_verify(gpu_lib, inp, num_splits=S, split_policy=gpu_lib.SPLIT_BY_LENGTH)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, f"by length {case}")
+    out_p, lse_p = run_verify(gpu_lib, inp, num_splits=S)
+    compare(out, lse, out_p.float().cpu().numpy().astype(np.float64),
+            lse_p.cpu().numpy().astype(np.float64), "by length vs per sequence")
+
+
+@pytest.mark.parametrize("batch", [64, 65])
+def test_split_by_length_batch_limit(gpu_lib, batch):
+    """64 sequences of random lengths use the plan by length; 65 fall back to
+    the per-sequence plan (bit for bit the per-sequence call)."""
+    rng = np.random.default_rng(batch)
+    lens = [int(x) for x in rng.integers(3, 6000, size=batch)]
+    _say(f"split by length, {batch} sequences")
+    inp = make_inputs(lens, 3, 12, "fp8", seed=batch, device="cuda")
+    out, lse = run_verify(gpu_lib, inp, split_policy=gpu_lib.SPLIT_BY_LENGTH)
+    out_p, lse_p = run_verify(gpu_lib, inp)
+    if batch > 64:
+        assert torch.equal(out, out_p) and torch.equal(lse, lse_p)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, f"{batch} sequences by length")
+
+
+def test_split_by_length_equal_lengths_bitwise(gpu_lib):
+    """With equal lengths the plan by length is the per-sequence plan: the
+    same bits."""
+    inp = make_inputs([3000] * 4, 3, 12, "fp8", seed=41, device="cuda")
+    out, lse = run_verify(gpu_lib, inp, num_splits=16, split_policy=gpu_lib.SPLIT_BY_LENGTH)
+    out_p, lse_p = run_verify(gpu_lib, inp, num_splits=16)
+    assert torch.equal(out, out_p) and torch.equal(lse, lse_p)
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c6"])
+def test_workload_split_by_length(gpu_lib, cfg):
+    """The ragged workloads at full size with the plan by length: every
+    sequence against the oracle."""
+    _say(f"workload {cfg} by length")
+    inp = make_config(cfg, device="cuda")
+    hint = workloads.CONFIGS[cfg]["seq_hi"]
+    out, lse = run_verify(gpu_lib, inp, max_seq_len_hint=hint, split_policy=gpu_lib.SPLIT_BY_LENGTH)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, f"{cfg} by length")
+
+
 def test_split_then_merge_equals_verify(gpu_lib):
     """mla_split followed by mla_merge on the same S is the verify call's own
     two launches: bitwise the same output and lse."""
