@@ -526,7 +526,13 @@ def main():
     ragged = cfg["seq_lo"] != cfg["seq_hi"]
     policy_name = args.split_policy
     if policy_name == "auto":
-        policy_name = "by-length" if ragged else "per-sequence"
+        # by length for unequal lengths when the per-sequence plan runs at most
+        # five rounds of workgroups (beyond that the rounds balance the work:
+        # at eight rounds, B = 64 FP8 verify, both plans take the same time)
+        rows = first.num_q * first.heads
+        rblock = 64 if (first.kv_dtype == "fp8" and rows > 32) else (16 if rows <= 16 else 48)
+        wgs = S * first.batch * -(-rows // rblock)
+        policy_name = "by-length" if (ragged and wgs <= 5 * 256) else "per-sequence"
     policy = mla.SPLIT_BY_LENGTH if policy_name == "by-length" else mla.SPLIT_PER_SEQUENCE
     # the split and merge of the plan by length run only inside mla_verify:
     # the kernel legs below are timed together, as the layer-step
