@@ -498,6 +498,25 @@ def test_split_by_length_batch_limit(gpu_lib, batch):
     compare(out, lse, ro, rl, f"{batch} sequences by length")
 
 
+@pytest.mark.parametrize("S", [192, 193])
+def test_split_by_length_slot_limit(gpu_lib, S):
+    """64 sequences with S = 192 splits give 12,288 slots: the longest run of
+    one sequence (12,225 slots) is the most the merge's weight table takes,
+    and the plan by length is used; at S = 193 it is past that and the call
+    uses the per-sequence plan (bit for bit)."""
+    rng = np.random.default_rng(S)
+    lens = [int(x) for x in rng.integers(3, 400, size=64)]
+    lens[7] = 20000
+    _say(f"split by length at the slot limit, S = {S}")
+    inp = make_inputs(lens, 3, 12, "fp8", seed=S, device="cuda")
+    out, lse = run_verify(gpu_lib, inp, num_splits=S, split_policy=gpu_lib.SPLIT_BY_LENGTH)
+    out_p, lse_p = run_verify(gpu_lib, inp, num_splits=S)
+    if S > 192:
+        assert torch.equal(out, out_p) and torch.equal(lse, lse_p)
+    ro, rl, _ = oracle_out(inp)
+    compare(out, lse, ro, rl, f"S={S} by length")
+
+
 def test_split_by_length_equal_lengths_bitwise(gpu_lib):
     """With equal lengths the plan by length is the per-sequence plan: the
     same bits."""
