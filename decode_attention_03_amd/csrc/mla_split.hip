@@ -824,68 +824,6 @@ static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 1
               pv_voff(2, 3) == 23136 && pv_voff(3, 0) == 96 && pv_voff(3, 1) == 4672 &&
               pv_voff(3, 2) == 18528 && pv_voff(3, 3) == 23104, "value offsets");
 
-// A lane's query fragments from the block staged in LDS (see the prologue of
-// split_kernel_f8x64): a[c] is the address of chunk pair c at the lane's
-// first k-step, and k-step ks lies 128 ks bytes further.  NKS = 5 or 4 steps.
-template <int NKS>
-__device__ __forceinline__ void read_q_f8(const uint32_t (&a)[4], u32x4 (&v)[5][4]) {
-  static_assert(NKS == 4 || NKS == 5, "four or five k-steps");
-  if constexpr (NKS == 5) {
-    asm volatile(
-        "ds_read_b128 %0, %20\n\t"
-        "ds_read_b128 %1, %21\n\t"
-        "ds_read_b128 %2, %22\n\t"
-        "ds_read_b128 %3, %23\n\t"
-        "ds_read_b128 %4, %20 offset:128\n\t"
-        "ds_read_b128 %5, %21 offset:128\n\t"
-        "ds_read_b128 %6, %22 offset:128\n\t"
-        "ds_read_b128 %7, %23 offset:128\n\t"
-        "ds_read_b128 %8, %20 offset:256\n\t"
-        "ds_read_b128 %9, %21 offset:256\n\t"
-        "ds_read_b128 %10, %22 offset:256\n\t"
-        "ds_read_b128 %11, %23 offset:256\n\t"
-        "ds_read_b128 %12, %20 offset:384\n\t"
-        "ds_read_b128 %13, %21 offset:384\n\t"
-        "ds_read_b128 %14, %22 offset:384\n\t"
-        "ds_read_b128 %15, %23 offset:384\n\t"
-        "ds_read_b128 %16, %20 offset:512\n\t"
-        "ds_read_b128 %17, %21 offset:512\n\t"
-        "ds_read_b128 %18, %22 offset:512\n\t"
-        "ds_read_b128 %19, %23 offset:512\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]),
-          "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[2][0]), "=&v"(v[2][1]),
-          "=&v"(v[2][2]), "=&v"(v[2][3]), "=&v"(v[3][0]), "=&v"(v[3][1]), "=&v"(v[3][2]),
-          "=&v"(v[3][3]), "=&v"(v[4][0]), "=&v"(v[4][1]), "=&v"(v[4][2]), "=&v"(v[4][3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
-  } else {
-    asm volatile(
-        "ds_read_b128 %0, %16\n\t"
-        "ds_read_b128 %1, %17\n\t"
-        "ds_read_b128 %2, %18\n\t"
-        "ds_read_b128 %3, %19\n\t"
-        "ds_read_b128 %4, %16 offset:128\n\t"
-        "ds_read_b128 %5, %17 offset:128\n\t"
-        "ds_read_b128 %6, %18 offset:128\n\t"
-        "ds_read_b128 %7, %19 offset:128\n\t"
-        "ds_read_b128 %8, %16 offset:256\n\t"
-        "ds_read_b128 %9, %17 offset:256\n\t"
-        "ds_read_b128 %10, %18 offset:256\n\t"
-        "ds_read_b128 %11, %19 offset:256\n\t"
-        "ds_read_b128 %12, %16 offset:384\n\t"
-        "ds_read_b128 %13, %17 offset:384\n\t"
-        "ds_read_b128 %14, %18 offset:384\n\t"
-        "ds_read_b128 %15, %19 offset:384\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]),
-          "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[2][0]), "=&v"(v[2][1]),
-          "=&v"(v[2][2]), "=&v"(v[2][3]), "=&v"(v[3][0]), "=&v"(v[3][1]), "=&v"(v[3][2]),
-          "=&v"(v[3][3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
-    v[4][0] = v[4][1] = v[4][2] = v[4][3] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
 // Eight waves in two groups of four; group g owns query rows 32g..32g+31 and
 // waves 4g..4g+3, and SIMD k runs wave k of group 0 and wave k of group 1.
 // Within a group, wave v = w & 3:
@@ -948,7 +886,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   __shared__ __attribute__((aligned(16))) f32x4 xbuf[kF8Waves][2][2][64];
   // per group and row: {f of block 0, f of block 1, fp32 weight sum of block 0, of block 1}
   __shared__ __attribute__((aligned(16))) f32x4 blk[2][32];
-  __shared__ float qmax[kF8Waves][32];
+  __shared__ float qsc[64];   // 2^-e of each query row of the block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1068,11 +1006,20 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // arrive as zeros.  Chunk j of row r sits at chunk (j & ~7) | ((j ^ r) & 7)
   // of its LDS row, so the 16 rows one ds_read_b128 phase reads fall in
   // distinct bank groups (two-way at most).
+  // Each row is converted once per workgroup, in place: wave w takes rows
+  // 8w .. 8w + 7, eight lanes a row and nine 16-byte chunks a lane (chunks
+  // l % 8 + 8i), finds the row's exponent e with the other seven lanes of
+  // the row, and writes the two FP8 terms over the row's own 1,152 bytes:
+  // term t at byte 576 t of the row, its 16-byte chunk x at chunk
+  // x ^ ((r / 2) % 4) (rows 1,152 bytes apart fall on two bank offsets; the
+  // XOR, inside each group of four chunks, spreads 16 rows over 8 of them).
+  // A wave writes only the rows it has itself read, so no barrier sits
+  // between the reads and the writes.  Waves whose rows are all padding only
+  // write zeros.
   i32x8 q1[5], q2[5];
-  float q_unscale;
   int ptA, ptB;   // group 1: page-table entries of the next two tiles to copy
+  const int pt0 = pt_load(grp);   // page v4 of the group's first tile
   {
-    const int pt0 = pt_load(grp);
     ptA = pt_load(2);
     ptB = pt_load(3);
     // The probability terms and block data read by each group's first PV
@@ -1088,68 +1035,82 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
     lds_barrier();   // every wave's query loads have landed
-    u32x4 qv[5][4];
     {
-      const int lr = 32 * grp + r32;   // row within the block
-      const uint32_t rb = (uint32_t)(uintptr_t)LDS_PTR(uint8_t, qlds + lr * (2 * kLatent) + 128 * ks0);
-      uint32_t qa[4];
+      const int crow = 8 * w + (lane >> 3);          // the lane's row within the block
+      uint8_t* const rowp = qlds + crow * (2 * kLatent);
+      const int sw = (crow >> 1) & 3;
+      u32x2 th[9], tl[9];                            // terms of the lane's nine chunks
+      float isc = 1.f;
+      if (8 * w < min(64, R - 64 * wc.z)) {
+        u32x4 c[9];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qa[c] = rb + 16u * (uint32_t)((4 * h + c) ^ (lr & 7));
-      if (dh) read_q_f8<4>(qa, qv);
-      else read_q_f8<5>(qa, qv);
-    }
-    // largest magnitude of the lane's values: the magnitude bits of bf16
-    // values order as integers, two per dword (packed 16-bit maximum)
-    u16x2 mk = {0, 0};
+        for (int i = 0; i < 9; ++i) c[i] = *(const u32x4*)(rowp + 16 * (8 * i + ((lane ^ crow) & 7)));
+        // largest magnitude of the row: the magnitude bits of bf16 values
+        // order as integers, two per dword (packed 16-bit maximum)
+        u16x2 mk = {0, 0};
 #pragma unroll
-    for (int ks = 0; ks < 5; ++ks)
+        for (int i = 0; i < 9; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+          for (int k = 0; k < 4; ++k)
+            mk = __builtin_elementwise_max(mk, __builtin_bit_cast(u16x2, c[i][k] & 0x7FFF7FFFu));
+        float mx = __uint_as_float((uint32_t)max(mk[0], mk[1]) << 16);
+        mx = xor_max(xor_max(xor_max(mx, 1), 2), 4);   // the row's eight lanes
+        int e = 0;
+        if (mx > 0.f) {
+          const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126;  // mx = m * 2^ex, m in [0.5, 1)
+          e = min(max(7 - ex, -100), 100);
+        }
+        isc = pow2f(-e);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          mk = __builtin_elementwise_max(mk, __builtin_bit_cast(u16x2, qv[ks][c][k] & 0x7FFF7FFFu));
-    float mx = __uint_as_float((uint32_t)max(mk[0], mk[1]) << 16);
-    mx = max32(mx);                                 // the two lanes holding this row
-    if (h == 0) qmax[w][r32] = mx;
-    lds_barrier();   // also: every wave has read the staged query
-    if (grp == 1) {
-      issue_part(1, pt0, I0{}, I9{});
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    mx = fmaxf(qmax[w][r32], qmax[w ^ 2][r32]);     // the other half of the dims
-    int e = 0;
-    if (mx > 0.f) {
-      const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126;  // mx = m * 2^ex, m in [0.5, 1)
-      e = min(max(7 - ex, -100), 100);
-    }
-    q_unscale = pow2f(-e);
+        for (int i = 0; i < 9; ++i) {
+          int h0, l0, h1, l1;
+          split4_bf16_fp8(c[i][0], c[i][1], isc, h0, l0);
+          split4_bf16_fp8(c[i][2], c[i][3], isc, h1, l1);
+          th[i] = u32x2{(uint32_t)h0, (uint32_t)h1};
+          tl[i] = u32x2{(uint32_t)l0, (uint32_t)l1};
+        }
+      } else {
 #pragma unroll
-    for (int ks = 0; ks < 5; ++ks) {
-      // dh = 1 has four steps: its fifth query terms are zeros (qv[4] = 0)
-      i32x8 hi8, lo8;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 v = qv[ks][c];
-        int hh, ll;
-        split4_bf16_fp8(v[0], v[1], q_unscale, hh, ll);
-        hi8[2 * c] = hh;
-        lo8[2 * c] = ll;
-        split4_bf16_fp8(v[2], v[3], q_unscale, hh, ll);
-        hi8[2 * c + 1] = hh;
-        lo8[2 * c + 1] = ll;
+        for (int i = 0; i < 9; ++i) th[i] = tl[i] = u32x2{0u, 0u};
       }
-      q1[ks] = hi8;
-      q2[ks] = lo8;
+      // bf16 chunk j = l % 8 + 8i holds dims 8j .. 8j + 7: bytes 8(j % 2) of
+      // FP8 chunk j / 2 = 4i + (l % 8) / 2 of each term
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        uint8_t* const p = rowp + 16 * (4 * i + (((lane & 7) >> 1) ^ sw)) + 8 * (lane & 1);
+        *(u32x2*)p = th[i];
+        *(u32x2*)(p + kLatent) = tl[i];
+      }
+      if ((lane & 7) == 0) qsc[crow] = isc;
+    }
+    lds_barrier();   // every row's terms and scale are in place
+    {
+      const int lr = 32 * grp + r32;                  // the lane's fragment row
+      const uint8_t* const fb = qlds + lr * (2 * kLatent) + 64 * ks0;
+      const int sw = (lr >> 1) & 3;
+      const int o0 = 16 * ((2 * h) ^ sw), o1 = 16 * ((2 * h + 1) ^ sw);
+      auto frag = [&](int off) -> i32x8 {
+        const u32x4 x0 = *(const u32x4*)(fb + off + o0);
+        const u32x4 x1 = *(const u32x4*)(fb + off + o1);
+        return __builtin_bit_cast(i32x8, u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+      };
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        q1[ks] = frag(64 * ks);
+        q2[ks] = frag(64 * ks + kLatent);
+      }
+      // dh = 1 has four k-steps: its fifth query terms are zeros
+      q1[4] = dh ? i32x8{} : frag(256);
+      q2[4] = dh ? i32x8{} : frag(256 + kLatent);
     }
   }
   // scale into the log2 domain of the scores this lane handles in the
-  // softmax: row 16dh + l % 16 of the group (q_unscale is per row, held by
-  // lane l for row l % 32)
-  float cs;
-  {
-    const float c = a.score_scale_log2 * q_unscale;
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(c), __float_as_uint(c), false, false);
-    cs = __uint_as_float(dh ? r[1] : r[0]);
+  // softmax: row 16dh + l % 16 of the group
+  const float cs = a.score_scale_log2 * qsc[32 * grp + 16 * dh + (lane & 15)];
+  lds_barrier();   // every wave has read its query terms
+  if (grp == 1) {
+    issue_part(1, pt0, I0{}, I9{});
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Integer reference maximum of row r32 of this wave's group (log2 units),
@@ -1472,8 +1433,13 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     __builtin_amdgcn_s_setprio(0);
   };
   if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // A group whose 32 rows all lie past Q*H (group 1 of the last row block
+  // when Q*H is an odd multiple of 32) does no matrix or softmax work: its
+  // waves only take part in the barriers and issue their share of the copies.
+  const bool live = 64 * wc.z + 32 * grp < R;
   for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
     begin(hs);
+    if (!live) continue;
     const int st = hs - grp;
     if (st >= 0 && (st & 1) == 0) {
       mfma_phase(st >> 1);
