@@ -530,7 +530,7 @@ def main():
         # five rounds of workgroups (beyond that the rounds balance the work:
         # at eight rounds, B = 64 FP8 verify, both plans take the same time)
         rows = first.num_q * first.heads
-        rblock = 64 if (first.kv_dtype == "fp8" and rows > 32) else (16 if rows <= 16 else 48)
+        rblock = 64 if rows > 32 else (16 if rows <= 16 else 48)
         wgs = S * first.batch * -(-rows // rblock)
         policy_name = "by-length" if (ragged and wgs <= 5 * 256) else "per-sequence"
     policy = mla.SPLIT_BY_LENGTH if policy_name == "by-length" else mla.SPLIT_PER_SEQUENCE
@@ -657,8 +657,8 @@ def main():
     # executed MFMA work of the split kernel (padded rows, two-term fp8 operands)
     fp8 = first.kv_dtype == "fp8"
     rows = first.num_q * first.heads
-    # row blocks: 64 for the fp8 kernel (above 32 rows), else 16 or 48
-    rblock = 64 if (fp8 and rows > 32) else 16 if rows <= 16 else 48
+    # row blocks: 64 above 32 rows (the eight-wave kernels), else 16 or 48
+    rblock = 64 if rows > 32 else 16 if rows <= 16 else 48
     exec_rows = rblock * -(-rows // rblock)
     terms = 2 if (fp8 and rows > 32) else 1
     positions = sum(int(l.seq_lens.sum().item()) for l in layers) / n_layers

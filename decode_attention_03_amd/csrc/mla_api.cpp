@@ -71,10 +71,10 @@ int32_t choose_splits(const mla_params* p) {
   const int64_t pages = (max_len + mla::kPage - 1) / mla::kPage;
   const int64_t page_bytes = (int64_t)mla::kPage * mla::kLatent * (p->kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 2);
   const int64_t pages_per_split = kSplitBytes / page_bytes;   // 128 FP8 or 64 bf16 pages
-  // query rows are processed in blocks (64 rows for FP8 verify, else 48 or
-  // 16), each a workgroup of its own over the same split
+  // query rows are processed in blocks (64 rows above 32, else 48 or 16),
+  // each a workgroup of its own over the same split
   const int64_t rows = (int64_t)p->num_q_tokens * p->num_heads;
-  const int64_t rblock = (p->kv_dtype == MLA_KV_FP8_E4M3 && rows > 32) ? 64 : (rows <= 16 ? 16 : 48);
+  const int64_t rblock = rows > 32 ? 64 : (rows <= 16 ? 16 : 48);
   const int64_t units = (int64_t)p->batch * ((rows + rblock - 1) / rblock);
   int64_t s = (pages + pages_per_split - 1) / pages_per_split;
   int64_t fill = (kComputeUnits + units - 1) / units;

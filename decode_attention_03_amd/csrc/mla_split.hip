@@ -174,7 +174,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m)); }
 // x combined with the value of lane l ^ 32 (a VALU lane swap, no LDS round trip)
 __device__ __forceinline__ float max32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -184,7 +183,6 @@ __device__ __forceinline__ float sum32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
 // x combined with the value of lane l ^ 16 (a VALU row swap); both lanes of
 // a pair add in the same order
 __device__ __forceinline__ float max16(float x) {
@@ -194,6 +192,28 @@ __device__ __forceinline__ float max16(float x) {
 __device__ __forceinline__ float sum16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum / sum over each aligned group of eight lanes, with DPP moves
+// (quad permutations for lane ^ 1 and lane ^ 2, then the mirror inside each
+// half-row of eight lanes): three VALU steps, no LDS round trip.  Every lane of
+// a group ends with the same value (each step combines two equal-order pairs).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7 - i within each group of eight
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  return fmaxf(x, dpp_f<kDppHalfMirror>(x));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x = x + dpp_f<kDppXor1>(x);
+  x = x + dpp_f<kDppXor2>(x);
+  return x + dpp_f<kDppHalfMirror>(x);
 }
 
 // 8 FP8 E4M3FN codes (two dwords) -> 8 bf16 (exact).
@@ -480,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         sv[i] = ok ? s[i] * c2 : kNegInf;
         mx = fmaxf(mx, sv[i]);
       }
-      mx = xor_max(xor_max(mx, 16), 32);
+      mx = max32(max16(mx));
       if (g == 0) red_max[w][r16] = mx;
       lds_barrier();
 
@@ -496,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         pb[i] = (__bf16)p;
         ps += p;
       }
-      ps = xor_sum(xor_sum(ps, 16), 32);
+      ps = sum32(sum16(ps));
       if (g == 0) red_sum[w][r16] = ps;
       *(bf16x4*)(p_lds + r16 * kPRB + (16 * w + 4 * g) * 2) = pb;
       lds_barrier();
@@ -540,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
               mx = fmaxf(mx, v);
             }
           }
-        mx = xor_max(mx, 32);
+        mx = max32(mx);
         const float mA = (mx > m_runA + kSlack) ? mx : m_runA;   // lazy rescale
         if (w == 0 && h == 0) red_max[0][r32] = mA;
         // this wave writes the probabilities of its half of the tile positions
@@ -559,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
           const int sp = base / 16, q = (base % 16) / 4;
           *(bf16x4*)(p_lds + r32 * kPRB + (32 * sp + 8 * q + 4 * h) * 2) = pb;
         }
-        ps = xor_sum(ps, 32);
+        ps = sum32(ps);
         if (h == 0) red_sum[w][r32] = ps;
       } else {
         f32x4 s[NS16];
@@ -588,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
             mx = fmaxf(mx, v);
           }
         }
-        mx = xor_max(xor_max(mx, 16), 32);
+        mx = max32(max16(mx));
         const float mB = (mx > m_runB + kSlack) ? mx : m_runB;   // lazy rescale
         if (w == 2 && g == 0) red_max[2][rowB] = mB;
         float ps = 0.f;
@@ -605,7 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
           }
           *(bf16x4*)(p_lds + rowB * kPRB + (16 * sp + 4 * g) * 2) = pb;
         }
-        ps = xor_sum(xor_sum(ps, 16), 32);
+        ps = sum32(sum16(ps));
         if (g == 0) red_sum[w][rowB] = ps;
       }
       lds_barrier();
@@ -1054,7 +1074,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
           for (int k = 0; k < 4; ++k)
             mk = __builtin_elementwise_max(mk, __builtin_bit_cast(u16x2, c[i][k] & 0x7FFF7FFFu));
         float mx = __uint_as_float((uint32_t)max(mk[0], mk[1]) << 16);
-        mx = xor_max(xor_max(xor_max(mx, 1), 2), 4);   // the row's eight lanes
+        mx = max8(mx);   // the row's eight lanes
         int e = 0;
         if (mx > 0.f) {
           const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126;  // mx = m * 2^ex, m in [0.5, 1)
@@ -1492,6 +1512,383 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// bf16 KV with more than 32 query rows (speculative verify): the schedule of
+// split_kernel_f8x64 on bf16 operands.  Eight waves in two groups of four;
+// group g owns query rows 32g .. 32g + 31 of the 64-row block (r = j*H + h),
+// SIMD k runs wave k of each group, and the groups run one phase apart, so on
+// every SIMD one wave issues MFMAs while the other runs the softmax:
+//   phase E(i): group 0: PV(i-1), QK(i)   | group 1: softmax(i-1)
+//   phase O(i): group 0: softmax(i)       | group 1: PV(i-1), QK(i)
+// A tile is 32 positions (two pages, 36,864 bytes), three tiles in a ring.
+// Within a group, wave v = w & 3:
+//   QK:      S^T = K Q^T over the dimension quarter 144v .. 144v + 143 of the
+//            tile's 32 positions: nine v_mfma_f32_32x32x16_bf16 against query
+//            fragments held in 36 registers; the four partial tiles go to LDS;
+//   softmax: rows 8v .. 8v + 7 of the group, eight lanes a row and four
+//            positions a lane: the four partials added, the row's running
+//            maximum (lazy, as in split_kernel) and sum kept by those lanes,
+//            the probabilities (bf16) and the row's rescale factor for the
+//            output written to LDS;
+//   PV:      output columns 128v .. 128v + 127 of the group's 32 rows; the
+//            value operand is read transposed from the tile in the MFMA phase
+//            that scores it and held in registers until the next one, so a
+//            tile is read only in E(i) and O(i) and buffer (i + 2) % 3 can be
+//            refilled from the start of E(i).
+// The KV bytes reach the bf16 MFMAs as stored; every KV byte crosses HBM once.
+template <bool FINAL>
+__global__ __launch_bounds__(kF8Threads, 1) void split_kernel_b16x64(SplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using G = KvGeom<false>;
+  constexpr int kNBuf = 3;
+  constexpr int kTP = 32;                                // positions per tile
+  constexpr int kTPages = kTP / kPage;                   // 2
+  constexpr int kTileB = kTPages * G::kPageB;            // 36,864
+  constexpr int kRangeLoads = G::kPageB / 1024 / 2;      // 9: a wave's half of a page
+  constexpr int kPRB = kTP * 2 + 16;                     // bytes per bf16 probability row (+skew)
+  // one wave's partial-score tile in LDS: 64 lanes x 64 bytes, lanes 32..63
+  // 128 bytes further (see send_scores)
+  constexpr int kXB = 64 * 64 + 128;
+  // the reference maximum moves when a tile maximum passes it by more than
+  // 2^kSlack (bf16 probabilities up to 2^8, far from overflow)
+  constexpr float kSlack = 8.f;
+
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][32 * kPRB];   // [group][row][position]
+  __shared__ __attribute__((aligned(16))) uint8_t xbuf[2][4][kXB];       // [group][wave][...]
+  __shared__ float alpha_lds[2][32];                                     // output rescale per row
+  __shared__ float rowstat[2][32][2];                                    // final maximum and sum per row
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const int grp = w >> 2;
+  const int v4 = w & 3;
+  const int H = a.heads;
+  const int R = a.num_q * H;
+  const WgCoord wc = split_coord(a, (R + 63) / 64);
+  const int split = wc.split;
+  const int b = wc.b;
+  const int myrow = 64 * wc.z + 32 * grp + r32;
+
+  // seq_lens[b] first (a scalar load), then the query block's loads: the
+  // workgroup's 64 query rows (1,152 bytes each) are staged once in KV
+  // buffers 1 and 2 by direct-to-LDS loads, chunk j of row r at chunk
+  // (j & ~7) | ((j ^ r) & 7) of its LDS row; rows past Q*H lie outside the
+  // buffer range and arrive as zeros.
+  const int L = kDebug ? debug_seq_len(a.seq_lens[b], a.num_q, a.max_blocks, a.debug_flags) : a.seq_lens[b];
+  uint8_t* const qlds = kv_lds + kTileB;
+  {
+    const int nrows = min(64, R - 64 * wc.z);
+    const u32x4 qrsrc = buffer_rsrc(a.q + ((int64_t)b * R + 64 * wc.z) * kLatent, nrows * 2 * kLatent);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int slot = 64 * (w + 8 * i) + lane;   // 16-byte LDS slot of this lane
+      const int r = slot / 72, x = slot - 72 * (slot / 72);
+      const uint32_t src = 16u * (uint32_t)(72 * r + (x ^ (r & 7)));
+      copy16_to_lds(qrsrc, src, lds_addr(qlds + 1024 * (w + 8 * i)));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int P = (L + kPage - 1) / kPage;
+  const int S = wc.nsplit;
+  const int pq = P / S, pr = P - pq * S;
+  const int p0 = split * pq + (split * pr) / S;
+  const int p1 = (split + 1) * pq + ((split + 1) * pr) / S;
+  const int ntiles = (p1 - p0 + kTPages - 1) / kTPages;
+
+  // opaque copy of the lane index (see split_kernel_f8x64)
+  auto lane_now = [&]() -> int {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+
+  // ---- a2: copies.  Tile T goes to LDS buffer T % 3.  Wave (g, v) copies
+  // half v % 2 of page v / 2 of the tile (loads 9 (v % 2) .. + 8 of the
+  // page's eighteen one-KiB loads): tile 0 whole by group 0 in the prologue,
+  // tile 1 whole by group 1 once the staged query has been read, each tile
+  // T >= 2 shared by both groups during their softmax phases two tiles
+  // ahead (group 1 the first kLoads1 loads of each range at E(T - 2), group
+  // 0 the rest at O(T - 2)).  Pages outside the split and positions past
+  // seq_len lie outside the buffer range: the copy writes zeros.
+  constexpr int kLoads1 = 5;
+  const int cpage = v4 >> 1;
+  const int chalf = v4 & 1;
+  const __attribute__((address_space(4))) int32_t* pt_b =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + (int64_t)b * a.max_blocks);
+  const int plast = max(P - 1, 0);
+  auto pt_load = [&](int T) -> int { return pt_b[min(p0 + T * kTPages + cpage, plast)]; };
+  auto issue_part = [&](int T, int ptv, auto C0, auto C1) {
+    constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value;
+    const int gp = p0 + T * kTPages + cpage;
+    int blk = __builtin_amdgcn_readfirstlane(ptv);
+    if constexpr (kDebug) blk = gp < p1 ? debug_page_id(blk, a.num_blocks, a.debug_flags) : 0;
+    const int bytes = gp < p1 ? min(kPage, L - gp * kPage) * G::kRowB : 0;
+    const u32x4 rsrc = buffer_rsrc(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB, bytes);
+    uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + cpage * G::kPageB;
+    // LDS slot s = 64c + lane of the page holds source chunk
+    // 72 row + (x ^ swz(row)) with row = s / 72, x = s % 72; as 72 is a
+    // multiple of 8 that is s ^ swz(s / 72) = s ^ (s / 144) (s < 1152), and
+    // s / 144 = d0 + (lane >= t) with d0 = 64c / 144, t = 144 (d0 + 1) - 64c.
+    static_assert(G::kChunksPerRow == 72, "bf16 page rows of 72 chunks");
+    const int ln = lane_now();
+    const uint32_t vb = 16u * (uint32_t)ln;
+#pragma unroll
+    for (int c = c0; c < c1; ++c) {
+      const int base = 64 * (kRangeLoads * chalf + c);   // first slot of the load (wave-uniform)
+      const int d0 = base / 144;
+      const int t = 144 * (d0 + 1) - base;
+      const uint32_t d = (uint32_t)d0 + ((t < 64 && ln >= t) ? 1u : 0u);
+      const uint32_t voff = (vb + 16u * (uint32_t)base) ^ (d << 4);
+      copy16_to_lds(rsrc, voff, lds_addr(dst + 16 * base));
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, kLoads1>;
+  using I9 = std::integral_constant<int, kRangeLoads>;
+
+  // ---- query fragments (B operand of S^T = K Q^T): row 32g + l % 32, dims
+  // 144v + 16ks + 8h .. + 7 (bf16 chunk 18v + 2ks + h), ks < 9.
+  u32x4 qf[9];
+  int ptA, ptB;   // page-table entries of the next two tiles this wave copies
+  const int pt0 = pt_load(grp);
+  {
+    ptA = pt_load(2);
+    ptB = pt_load(3);
+    // probabilities read by each group's first PV are zeros and its rescale
+    // factors ones (that PV adds nothing; published by the barrier below)
+    for (int i = tid; i < (int)(sizeof(p_lds) / 16); i += kF8Threads) ((u32x4*)p_lds)[i] = u32x4{};
+    if (tid < 64) alpha_lds[tid >> 5][tid & 31] = 1.f;
+    if (grp == 0) {
+      issue_part(0, pt0, I0{}, I9{});
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRangeLoads));   // this wave's query loads
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    lds_barrier();   // every wave's query loads have landed
+    const int lr = 32 * grp + r32;
+    const uint8_t* const qrow = qlds + lr * (2 * kLatent);
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      const int j = 18 * v4 + 2 * ks + h;
+      qf[ks] = *(const u32x4*)(qrow + 16 * ((j & ~7) | ((j ^ lr) & 7)));
+    }
+  }
+  lds_barrier();   // every wave has read the staged query
+  if (grp == 1) {
+    issue_part(1, pt0, I0{}, I9{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  const float c2 = a.score_scale_log2;
+  float m_run = kNegInf, l_run = 0.f;   // softmax rows 8v + l / 8 (all eight lanes of a row hold them)
+  f32x16 o[4];
+  u32x4 vfr[8];   // value fragments of the group's next PV: column tile i / 2, k-step i % 2
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) vfr[c] = u32x4{0u, 0u, 0u, 0u};
+  uint8_t* const pg = p_lds[grp];
+
+  // Partial scores to LDS.  Lane l holds row l % 32 and positions
+  // 8(i / 4) + 4h + i % 4 of the tile (32x32 MFMA output layout); 16-byte
+  // chunk q (elements 4q .. 4q + 3) goes to byte 64 l + 128 h + 16 (q ^ ((l / 4) % 4))
+  // of the wave's tile, which spreads both the writes and the softmax's
+  // reads (eight rows, both halves, four chunks) over distinct bank groups.
+  auto send_scores = [&](const f32x16& s) {
+    const int ln = lane_now();
+    uint8_t* const xp = xbuf[grp][v4] + 64 * ln + 128 * (ln >> 5);
+    const int sw = (ln >> 2) & 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(f32x4*)(xp + 16 * (q ^ sw)) = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+  };
+
+  // ---- a5: softmax of tile T for rows 8v .. 8v + 7 of the group.  Lane
+  // l = 8k + 4u + c takes row 8v + k, positions 8c + 4u .. + 3: element
+  // chunk c of source lane 8v + k + 32u of each of the group's four waves.
+  auto softmax = [&](int T) {
+    const int ln = lane_now();
+    const int k = ln >> 3, u = (ln >> 2) & 1, c = ln & 3;
+    const int sl = 8 * v4 + k + 32 * u;
+    const int xoff = 64 * sl + 128 * u + 16 * (c ^ ((sl >> 2) & 3));
+    float x[4];
+    {
+      const f32x4 a0 = *(const f32x4*)(xbuf[grp][0] + xoff);
+      const f32x4 a1 = *(const f32x4*)(xbuf[grp][1] + xoff);
+      const f32x4 a2 = *(const f32x4*)(xbuf[grp][2] + xoff);
+      const f32x4 a3 = *(const f32x4*)(xbuf[grp][3] + xoff);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = (a0[j] + a1[j]) + (a2[j] + a3[j]);
+    }
+    const int row = 8 * v4 + k;
+    const int pos0 = 8 * c + 4 * u;
+    const int tpos0 = (p0 + T * kTPages) * kPage;
+    const int tlim = (p1 - p0 - T * kTPages) * kPage;
+    float mx = kNegInf;
+    if (tlim >= kTP && tpos0 + kTP <= L - a.num_q + 1) {   // every row sees the whole tile
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] *= c2;
+        mx = fmaxf(mx, x[j]);
+      }
+    } else {
+      const int lim = L - a.num_q + (64 * wc.z + 32 * grp + row) / H + 1;
+      const int kvis = min(tlim, lim - tpos0) - pos0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = j < kvis ? x[j] * c2 : kNegInf;
+        mx = fmaxf(mx, x[j]);
+      }
+    }
+    mx = max8(mx);   // the row's eight lanes
+    const float mn = (mx > m_run + kSlack) ? mx : m_run;   // lazy rescale
+    const float al = (mn == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+    m_run = mn;
+    bf16x4 pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = (x[j] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(x[j] - mn);
+      pb[j] = (__bf16)p;
+      ps += p;
+    }
+    ps = sum8(ps);
+    l_run = l_run * al + ps;
+    *(bf16x4*)(pg + row * kPRB + 2 * pos0) = pb;
+    if ((ln & 7) == 0) alpha_lds[grp][row] = al;
+  };
+
+  // ---- MFMA phase T: QK(T) and PV(T - 1), then the value fragments of tile T.
+  // a4 key operand of k-step ks: position l % 32 of the tile (page
+  // (l / 16) % 2, row l % 16), dims 144v + 16ks + 8h .. + 7.
+  // a6 O^T[c][r] += V^T[c][t] P^T[t][r], columns 128v + 32ct + l % 32, k-step
+  // kk = positions 16kk + 8h .. + 7 (value operand: two transposed reads).
+  auto mfma_phase = [&](int T) {
+    __builtin_amdgcn_s_setprio(2);
+    const int ln = lane_now();
+    const int row = ln & 31;
+    const float al = alpha_lds[grp][row];
+    const uint8_t* const tile = kv_lds + (T % kNBuf) * kTileB;
+    const uint8_t* const kp = tile + ((ln >> 4) & 1) * G::kPageB;
+    auto kop8 = [&](int ks) -> bf16x8 {
+      return as_bf16x8(load_k8<false>(kp, ln & 15, 144 * v4 + 16 * ks + 8 * (ln >> 5)));
+    };
+    const uint8_t* const pp = pg + row * kPRB + 16 * (ln >> 5);
+    const bf16x8 pf0 = as_bf16x8(*(const u32x4*)pp);
+    const bf16x8 pf1 = as_bf16x8(*(const u32x4*)(pp + 32));
+    // all nine key operands requested up front: the score MFMAs then wait
+    // only for the first, not for an LDS round trip each
+    bf16x8 kr[9];
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) kr[ks] = kop8(ks);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) s = mfma32(kr[ks], as_bf16x8(qf[ks]), s);
+    if (__any(al != 1.f)) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] *= al;
+    }
+    const int r16 = ln & 15;
+    const int cb = 128 * v4 + 16 * ((ln >> 4) & 1);
+    const int t0 = 8 * (ln >> 5);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      o[ct] = mfma32(as_bf16x8(vfr[2 * ct]), pf0, o[ct]);
+      o[ct] = mfma32(as_bf16x8(vfr[2 * ct + 1]), pf1, o[ct]);
+      vfr[2 * ct] = load_v8<false>(tile, t0, cb + 32 * ct, r16);
+      vfr[2 * ct + 1] = load_v8<false>(tile, 16 + t0, cb + 32 * ct, r16);
+      if (ct == 1) send_scores(s);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Half-steps hs = 0, 1, ...: E(i) = 2i, O(i) = 2i + 1, as in
+  // split_kernel_f8x64 (copy waits, barrier, copy issue at the start of each).
+  auto begin = [&](int hs) {
+    if ((hs & 1) == 0 && hs >= 2) {
+      if (grp) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRangeLoads - kLoads1));
+    }
+    lds_barrier();
+    if ((hs & 1) == 1 - grp) {
+      const int it = hs >> 1;
+      const int cur = (it & 1) ? ptB : ptA;
+      const int nxt = pt_load(it + 4);
+      if (grp) issue_part(it + 2, cur, I0{}, I1{});
+      else issue_part(it + 2, cur, I1{}, I9{});
+      if (it & 1) ptB = nxt;
+      else ptA = nxt;
+    }
+  };
+  if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // a group whose 32 rows all lie past Q*H only takes part in the barriers
+  // and the copies
+  const bool live = 64 * wc.z + 32 * grp < R;
+  for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
+    begin(hs);
+    if (!live) continue;
+    const int st = hs - grp;
+    if (st >= 0 && (st & 1) == 0) {
+      mfma_phase(st >> 1);
+    } else if (st >= 1) {
+      const int T = (st - 1) >> 1;
+      if (T < ntiles) softmax(T);
+    }
+  }
+
+  // every copy has landed (the epilogue reuses the KV buffers); the softmax
+  // lanes publish each row's maximum and sum
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  {
+    const int ln = lane_now();
+    if (live && (ln & 7) == 0) {
+      rowstat[grp][8 * v4 + (ln >> 3)][0] = m_run;
+      rowstat[grp][8 * v4 + (ln >> 3)][1] = l_run;
+    }
+  }
+  lds_barrier();
+  const float m_fin = rowstat[grp][r32][0];
+  const float l_fin = rowstat[grp][r32][1];
+
+  // ---- a7: epilogue, staged through the free KV buffers as in split_kernel_f8x64.
+  {
+    constexpr int kSRow = 256 + 16;
+    static_assert(kF8Waves * 32 * kSRow <= kNBuf * kTileB, "epilogue staging fits the KV buffers");
+    uint8_t* const stage = kv_lds + w * 32 * kSRow;
+    const float sc = l_fin > 0.f ? a.out_scale / l_fin : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(o[ct][4 * q + i] * sc);
+        *(bf16x4*)(stage + r32 * kSRow + 2 * (32 * ct + 8 * q + 4 * h)) = ov;
+      }
+    uint16_t* const dst = FINAL ? a.out : a.part_out;
+    const int64_t row0 = FINAL ? (int64_t)b * R : wc.slot * R;
+    const int cc = 8 * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const int grow = 64 * wc.z + 32 * grp + r;
+      const u32x4 v = *(const u32x4*)(stage + r * kSRow + 2 * cc);
+      if (grow < R) *(u32x4*)(dst + (row0 + grow) * kValue + 128 * v4 + cc) = v;
+    }
+  }
+  if (myrow < R && v4 == 0 && h == 0) {
+    const float lv = (l_fin > 0.f) ? (m_fin + log2f(l_fin)) * kLn2 : kNegInf;
+    if constexpr (FINAL) a.lse[(int64_t)b * R + myrow] = lv;
+    else a.part_lse[wc.slot * R + myrow] = lv;
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 template <int LAYOUT, bool FP8>
 hipError_t launch_layout(const SplitArgs& a, bool final_out, hipStream_t stream) {
   const int rows = a.num_q * a.heads;
@@ -1507,12 +1904,19 @@ hipError_t launch_layout(const SplitArgs& a, bool final_out, hipStream_t stream)
 template <bool FP8>
 hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) {
   const int rows = a.num_q * a.heads;
-  if (FP8 && rows > 32) {
+  if (rows > 32) {
     const dim3 grid((unsigned)(a.num_splits * a.batch * ((rows + 63) / 64)));
-    if (final_out)
-      hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kF8Threads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(split_kernel_f8x64<false>, grid, dim3(kF8Threads), 0, stream, a);
+    if constexpr (FP8) {
+      if (final_out)
+        hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kF8Threads), 0, stream, a);
+      else
+        hipLaunchKernelGGL(split_kernel_f8x64<false>, grid, dim3(kF8Threads), 0, stream, a);
+    } else {
+      if (final_out)
+        hipLaunchKernelGGL(split_kernel_b16x64<true>, grid, dim3(kF8Threads), 0, stream, a);
+      else
+        hipLaunchKernelGGL(split_kernel_b16x64<false>, grid, dim3(kF8Threads), 0, stream, a);
+    }
     return hipGetLastError();
   }
   if (rows <= 16) return launch_layout<kLayout16, FP8>(a, final_out, stream);
@@ -1525,7 +1929,7 @@ int64_t split_work_items(const SplitArgs& a, bool fp8) {
   // the grids of launch_dtype / launch_layout
   const int64_t rows = (int64_t)a.num_q * a.heads;
   const int64_t units = (int64_t)a.num_splits * a.batch;
-  if (fp8 && rows > 32) return units * ((rows + 63) / 64) * kF8Threads;
+  if (rows > 32) return units * ((rows + 63) / 64) * kF8Threads;
   const int64_t rpad = rows <= 16 ? 16 : 48;
   return units * ((rows + rpad - 1) / rpad) * kThreads;
 }
