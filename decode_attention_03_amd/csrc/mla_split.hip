@@ -1344,18 +1344,23 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // 2 ntiles + 2 half-steps, each with one workgroup barrier.  Tile 0 (group
   // 0's prologue copies) has landed before the loop; tile 1 (group 1's) only
   // before E(1).
-  // Start of a half-step.  Group 1 copies at even half-steps (hs = 0 and the
-  // starts of its softmax phases), group 0 at odd ones (its softmax phases).
-  // A group's vector-memory order is its share of tiles 2, 3, 4 ... (group
-  // 1: tile 1 whole before them): before E(T), T >= 1, its share of tile T
-  // must have landed while that of tile T + 1 may still be in flight.  The
-  // page-table entries are scalar loads, requested two tiles ahead.
+  // Start of a half-step: the copy waits and the workgroup barrier.  A
+  // group's vector-memory order is its share of tiles 2, 3, 4 ... (group 1:
+  // tile 1 whole before them): before E(T), T >= 1, its share of tile T must
+  // have landed while that of tile T + 1 may still be in flight.
   auto begin = [&](int hs) {
     if ((hs & 1) == 0 && hs >= 2) {
       if (grp) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
     }
     lds_barrier();
+  };
+  // End of a half-step: group 1 copies at even half-steps (hs = 0 and its
+  // softmax phases), group 0 at odd ones (its softmax phases), after the
+  // softmax work (issued first, a copy that stalls on a full memory queue
+  // would hold the softmax up).  The page-table entries are scalar loads,
+  // requested two tiles ahead.
+  auto copies = [&](int hs) {
     if ((hs & 1) == 1 - grp) {
       const int it = hs >> 1;
       const int cur = (it & 1) ? ptB : ptA;
@@ -1459,14 +1464,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const bool live = 64 * wc.z + 32 * grp < R;
   for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
     begin(hs);
-    if (!live) continue;
     const int st = hs - grp;
-    if (st >= 0 && (st & 1) == 0) {
+    if (live && st >= 0 && (st & 1) == 0) {
       mfma_phase(st >> 1);
-    } else if (st >= 1) {
+    } else if (live && st >= 1) {
       const int T = (st - 1) >> 1;
       if (T < ntiles) softmax(T);
     }
+    copies(hs);
   }
 
   // No copy may still be writing this workgroup's LDS when it ends, and the
@@ -1711,6 +1716,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_b16x64(SplitArgs a
   // l = 8k + 4u + c takes row 8v + k, positions 8c + 4u .. + 3: element
   // chunk c of source lane 8v + k + 32u of each of the group's four waves.
   auto softmax = [&](int T) {
+    __builtin_amdgcn_s_setprio(2);
     const int ln = lane_now();
     const int k = ln >> 3, u = (ln >> 2) & 1, c = ln & 3;
     const int sl = 8 * v4 + k + 32 * u;
@@ -1768,7 +1774,6 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_b16x64(SplitArgs a
   // a6 O^T[c][r] += V^T[c][t] P^T[t][r], columns 128v + 32ct + l % 32, k-step
   // kk = positions 16kk + 8h .. + 7 (value operand: two transposed reads).
   auto mfma_phase = [&](int T) {
-    __builtin_amdgcn_s_setprio(2);
     const int ln = lane_now();
     const int row = ln & 31;
     const float al = alpha_lds[grp][row];
@@ -1804,17 +1809,20 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_b16x64(SplitArgs a
       vfr[2 * ct + 1] = load_v8<false>(tile, 16 + t0, cb + 32 * ct, r16);
       if (ct == 1) send_scores(s);
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // Half-steps hs = 0, 1, ...: E(i) = 2i, O(i) = 2i + 1, as in
-  // split_kernel_f8x64 (copy waits, barrier, copy issue at the start of each).
+  // split_kernel_f8x64: copy waits and barrier at the start of each, copy
+  // issue at the end.  Here the softmax role is the longer one: it runs at
+  // raised priority (with its copies), the MFMA role at the normal one.
   auto begin = [&](int hs) {
     if ((hs & 1) == 0 && hs >= 2) {
       if (grp) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRangeLoads - kLoads1));
     }
     lds_barrier();
+  };
+  auto copies = [&](int hs) {
     if ((hs & 1) == 1 - grp) {
       const int it = hs >> 1;
       const int cur = (it & 1) ? ptB : ptA;
@@ -1831,14 +1839,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_b16x64(SplitArgs a
   const bool live = 64 * wc.z + 32 * grp < R;
   for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
     begin(hs);
-    if (!live) continue;
     const int st = hs - grp;
-    if (st >= 0 && (st & 1) == 0) {
+    if (live && st >= 0 && (st & 1) == 0) {
       mfma_phase(st >> 1);
-    } else if (st >= 1) {
+    } else if (live && st >= 1) {
       const int T = (st - 1) >> 1;
       if (T < ntiles) softmax(T);
     }
+    copies(hs);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // every copy has landed (the epilogue reuses the KV buffers); the softmax
