@@ -430,15 +430,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       // one buffer resource per page: the copy is bounds-checked to the page
       int blk = __builtin_amdgcn_readfirstlane(pt_row[page]);
       if constexpr (kDebug) blk = debug_page_id(blk, a.num_blocks, a.debug_flags);
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.kv + (int64_t)blk * G::kPageB), 0, G::kPageB, kBufferRsrcWord3);
+      const u32x4 rsrc = buffer_rsrc(a.kv + (int64_t)blk * G::kPageB, G::kPageB);
+      // issued from inline assembly (copy16_to_lds): seen by the compiler as
+      // LDS writes, these copies would make it wait for all of them (the
+      // next tile's included) before the LDS reads of the current tile; the
+      // waits for them are the explicit vmcnt waits at the top of the loop
 #pragma unroll
       for (int c = 0; c < kWaveLoads; ++c) {
         const uint32_t slot = wslot0 + 64 * c + lane;
         const uint32_t row = slot / G::kChunksPerRow;
         const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, dst + 1024 * c), 16,
-                                                 row * G::kRowB + x * 16, 0, 0, 0);
+        copy16_to_lds(rsrc, row * G::kRowB + x * 16, lds_addr(dst + 1024 * c));
       }
     } else {
 #pragma unroll
@@ -451,6 +453,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
   for (int T = 0; T < kNBuf - 1; ++T)
     if (T < ntiles) issue_tile(T);
+  // The query loads are waited for here, once, together with the first
+  // tiles' copies: at their first use inside the loop the compiler's wait
+  // (vmcnt(0), it does not count the copies) would come back in every
+  // iteration and hold each one up until the next tile had landed.
+#pragma unroll
+  for (int ks = 0; ks < kQRegs; ++ks) asm volatile("" ::"v"(qreg[ks]));
 
   const float c2 = a.score_scale_log2;
 
@@ -698,6 +706,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // buffers: every copy has landed, and the barrier below ends every wave's
   // last reads of them), so that a store instruction writes four whole
   // 256-byte row segments instead of 16 or 32 rows with 16-32 bytes each.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();
   {
     constexpr int kSRow = 256 + 16;   // staged row stride (bytes), skewed against bank conflicts
