@@ -325,29 +325,37 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   using G = KvGeom<FP8>;
   using KR = typename KRaw<FP8>::T;
   constexpr bool L16 = LAYOUT == kLayout16;
+  // bf16 KV with at most 16 rows (decode): 32-position tiles in a ring of
+  // four, so three tiles (110,592 bytes) are in flight while one is
+  // computed; each wave contracts half the dims of one page of the tile.
+  constexpr bool kHalf = L16 && !FP8;
   // Tile: 64 positions (4 pages), except 32 (2 pages) for bf16 with 48 rows,
-  // where LDS holds three bf16 tiles plus the partial-score exchange.
-  constexpr int TP = (!L16 && !FP8) ? 32 : 64;
+  // where LDS holds three bf16 tiles plus the partial-score exchange, and for
+  // bf16 with at most 16 rows (kHalf).
+  constexpr int TP = (!FP8 && (!L16 || kHalf)) ? 32 : 64;
   constexpr int TPG = TP / kPage;                  // pages per tile
   constexpr int kTileB = TPG * G::kPageB;
-  constexpr int kNBuf = L16 ? G::kNBuf : 3;
+  constexpr int kNBuf = kHalf ? 4 : (L16 ? G::kNBuf : 3);
   constexpr int kWaveLoads = kTileB / kWaves / 1024;   // 1 KiB DMA loads per wave per tile (9 or 18)
   constexpr int RPAD = L16 ? 16 : 48;
   constexpr int kPRB = TP * 2 + 16;                // LDS bytes per probability row
   constexpr int NS32 = TP / 32;                    // 32-position sub-tiles of the 32-row tile
   constexpr int NS16 = TP / 16;                    // 16-position sub-tiles of the 16-row tile
-  constexpr int kQRegs = 18;                       // query fragments held per wave
-  constexpr int kXFloats = L16 ? 1 : 16 * NS32;    // partial scores exchanged per lane
+  constexpr int kQRegs = kHalf ? 9 : 18;           // query fragments held per wave
+  // partial scores exchanged per lane
+  constexpr int kXFloats = kHalf ? 4 : (L16 ? 1 : 16 * NS32);
   // Lazy rescale: a row's reference maximum moves only when a tile maximum
   // exceeds it by more than 2^kSlack (bf16 probabilities up to 2^8 are exact
   // enough and far from overflow), which skips most output rescales.
   constexpr float kSlack = 8.f;
 
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[kNBuf * kTileB];
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[RPAD * kPRB];
+  // probabilities: one copy per wave with kHalf (each wave computes the whole
+  // tile's softmax for its own PV), else one shared copy
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[(kHalf ? kWaves : 1) * RPAD * kPRB];
   __shared__ float red_max[kWaves][RPAD];
   __shared__ float red_sum[kWaves][RPAD];
-  __shared__ __attribute__((aligned(16))) float xbuf[L16 ? 4 : kWaves * kXFloats * 64];
+  __shared__ __attribute__((aligned(16))) float xbuf[(L16 && !kHalf) ? 4 : kWaves * kXFloats * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kQRegs; ++ks) {
       int d0;
-      if (L16) d0 = 32 * ks + 8 * g;
+      if (L16) d0 = (kHalf ? 288 * (w >> 1) : 0) + 32 * ks + 8 * g;
       else d0 = t32 ? 288 * dh + 16 * ks + 8 * h : 288 * dh + 32 * (ks % 9) + 8 * g;
       const bool use = real && (L16 || t32 || ks < 9);
       qreg[ks] = use ? *(const u32x4*)(qp + d0) : u32x4{0, 0, 0, 0};
@@ -463,11 +471,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const float c2 = a.score_scale_log2;
 
   for (int it = 0; it < ntiles; ++it) {
-    // Wait for this wave's copy of tile `it`; a later tile may stay in flight.
-    if (kNBuf == 3 && it + 1 < ntiles && has_page(it + 1))
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // Wait for this wave's copy of tile `it`; later tiles may stay in flight
+    // (a wave copies nothing for a tile past its last page).
+    if constexpr (kNBuf == 4) {
+      if (has_page(it + 2)) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kWaveLoads));
+      else if (has_page(it + 1)) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    } else {
+      if (kNBuf == 3 && it + 1 < ntiles && has_page(it + 1))
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     uint8_t* tile = kv_lds + (it % kNBuf) * kTileB;
     {
       // zero the slots past seq_len among the rows this wave copied (last page only)
@@ -489,7 +504,61 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     const int tlim = (p1 - p0 - it * TPG) * kPage;  // tile slots inside the split
 
     float alphaA = 1.f, alphaB = 1.f;
-    if constexpr (L16) {
+    if constexpr (kHalf) {
+      // ---- a4/a5 (bf16, <= 16 rows): wave w contracts page w % 2 of the tile
+      // over dims 288 (w / 2) .. + 287 against the 16-row tile; after one
+      // exchange of the four partial tiles every wave holds the scores of
+      // all 32 positions (its lane r16 + 16 g: positions 4g + i of each
+      // page) and runs the tile's softmax itself, in the same order as the
+      // others, so all four keep the same running maximum and sum, and writes
+      // the probabilities to its own copy for its PV.
+      {
+        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        const uint8_t* pg = tile + (w & 1) * G::kPageB;
+        pipelined<9, 3, KR>([&](int ks) { return load_k8<FP8>(pg, r16, 288 * (w >> 1) + 32 * ks + 8 * g); },
+                            [&](int ks, KR raw) {
+                              if (ks & 1) s1 = mfma16(kop(raw), as_bf16x8(qreg[ks]), s1);
+                              else s0 = mfma16(kop(raw), as_bf16x8(qreg[ks]), s0);
+                            });
+        *(f32x4*)(xbuf + (w * 64 + lane) * 4) = s0 + s1;
+      }
+      lds_barrier();
+      float sv[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        // page pp: dims 0..287 from wave pp, dims 288..575 from wave pp + 2
+        const f32x4 lo = *(const f32x4*)(xbuf + (pp * 64 + lane) * 4);
+        const f32x4 hi = *(const f32x4*)(xbuf + ((pp + 2) * 64 + lane) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = 16 * pp + 4 * g + i;
+          const bool ok = tt < tlim && tpos0 + tt < limA;
+          sv[4 * pp + i] = ok ? (lo[i] + hi[i]) * c2 : kNegInf;
+          mx = fmaxf(mx, sv[4 * pp + i]);
+        }
+      }
+      mx = max32(max16(mx));
+      const float mA = (mx > m_runA + kSlack) ? mx : m_runA;   // lazy rescale
+      alphaA = (mA == m_runA) ? 1.f : __builtin_amdgcn_exp2f(m_runA - mA);
+      m_runA = mA;
+      uint8_t* const pme = p_lds + w * RPAD * kPRB;
+      float ps = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = sv[4 * pp + i];
+          const float pr = (v == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(v - mA);
+          pb[i] = (__bf16)pr;
+          ps += pr;
+        }
+        *(bf16x4*)(pme + r16 * kPRB + (16 * pp + 4 * g) * 2) = pb;
+      }
+      ps = sum32(sum16(ps));
+      l_runA = l_runA * alphaA + ps;
+    } else if constexpr (L16) {
       // ---- a4/a5 (<= 16 rows): wave w scores page w of the tile against the 16-row tile.
       float sv[4];
       f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -663,7 +732,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 
     // ---- a6: O^T[c][r] += V^T[c][t] P^T[t][r] for this wave's 128 columns.
     const int col0 = 128 * w;
-    if constexpr (L16) {
+    if constexpr (kHalf) {
+      // one 32-position k-step: probabilities 8g .. 8g + 7 of row r16 from
+      // this wave's own copy (written above by this wave: LDS is in order)
+      const bf16x8 pf = as_bf16x8(*(const u32x4*)(p_lds + w * RPAD * kPRB + r16 * kPRB + 16 * g));
+      pipelined<8, 4, KR>([&](int i) { return load_v8<FP8>(tile, 8 * g, col0 + 16 * i, r16); },
+                          [&](int i, KR raw) { o16a[i] = mfma16(kop(raw), pf, o16a[i]); });
+    } else if constexpr (L16) {
       bf16x8 pf[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
