@@ -32,12 +32,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 DEVICE_CODE = os.path.join(ROOT, "decode_attention_03_amd", "_build", "device_code.json")
 
 
-def _split_device_sha256():
-    """sha256 of the split kernels' gfx950 assembly in the current build (written
-    by the build next to the objects), or None if the build did not record it."""
+def _kernel_sha256(name):
+    """sha256 of one split kernel's gfx950 assembly in the current build (by its
+    demangled name, as the profiler reports it; written by the build next to
+    the objects), or None if the build did not record it."""
     if not os.path.exists(DEVICE_CODE):
         return None
-    return json.load(open(DEVICE_CODE)).get("mla_split.hip")
+    return json.load(open(DEVICE_CODE)).get("kernels", {}).get("mla_split.hip", {}).get(name)
 
 
 def _log(msg):
@@ -93,15 +94,15 @@ def _layers(cfg, device):
 
 def _profile_record(tag, num_splits, policy):
     """The committed counter summary of the split kernel for this workload, or
-    None when it is missing or was taken on other split-kernel device code (the
-    gfx950 assembly of the current build), another split count or another
-    split policy."""
+    None when it is missing or was taken on other device code of that kernel
+    (its gfx950 assembly in the current build), another split count or
+    another split policy."""
     path = os.path.join(PROFILES, f"split_traffic__{tag}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    dev = _split_device_sha256()
-    if dev is None or rec.get("split_device_sha256") != dev or rec.get("num_splits") != num_splits:
+    dev = _kernel_sha256(rec.get("kernel"))
+    if dev is None or rec.get("split_kernel_sha256") != dev or rec.get("num_splits") != num_splits:
         return None
     if rec.get("split_policy", "per-sequence") != policy:
         return None
@@ -150,8 +151,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
     """Writes profiles/kernel_stats__TAG.md, profiles/split_traffic__TAG.json/.md
     from rocprofv3 output of `bench.py --copy-calibration` runs (CPU only)."""
     import workloads
-    if _split_device_sha256() is None:
-        raise SystemExit("build the library first: the summary records the split kernels' "
+    if not os.path.exists(DEVICE_CODE):
+        raise SystemExit("build the library first: the summary records the split kernel's "
                          "device-code hash of the current build")
     stats = _read_csvs(trace_dir, "kernel_stats.csv")
     trace = _read_csvs(trace_dir, "kernel_trace.csv")
@@ -228,7 +229,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, tag):
         "config_key": cfg,
         "num_splits": S,
         "split_policy": _recorded_config(trace_dir).get("split_policy", "per-sequence"),
-        "split_device_sha256": _split_device_sha256(),
+        "split_kernel_sha256": _kernel_sha256(split_stat[0]["Name"]),
         "split_avg_us": round(split_avg_us, 3),
         "merge_avg_us": round(float(merge_stat[0]["AverageNs"]) / 1e3, 3) if merge_stat else None,
         "fetch_kib_per_dispatch": round(spl_f[0], 1),

@@ -57,17 +57,44 @@ def _run(cmd, verbose):
     return out
 
 
+def _demangle(names):
+    """Demangled C++ names (c++filt), or the names unchanged without it."""
+    try:
+        res = subprocess.run(["c++filt"], input="\n".join(names), stdout=subprocess.PIPE, text=True,
+                             check=True)
+        out = res.stdout.splitlines()
+        return out if len(out) == len(names) else list(names)
+    except (OSError, subprocess.CalledProcessError):
+        return list(names)
+
+
 def device_code_sha256(src, verbose=False):
     """sha256 of the gfx950 assembly hipcc emits for one kernel source, with the
     per-compilation unit id symbol (the only part that changes from one
-    compile of the same source to the next) normalised.  Host-only edits of a
-    source leave it unchanged, any change of its device code changes it."""
+    compile of the same source to the next) normalised, and the sha256 of
+    each kernel function's own assembly (label to end of function) by
+    demangled name.  Host-only edits of a source leave them unchanged; a
+    change of a kernel's device code changes its hash and the file's, and
+    leaves the hashes of the source's other kernels as they were."""
     with tempfile.TemporaryDirectory() as tmp:
         out = os.path.join(tmp, "dev.s")
         _run([HIPCC] + FLAGS + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out], verbose)
         text = open(out).read()
     text = re.sub(r"__hip_cuid_[0-9a-f]+", "__hip_cuid", text)
-    return hashlib.sha256(text.encode()).hexdigest()
+    bodies = {}
+    cur, lines = None, []
+    for line in text.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            cur, lines = m.group(1), []
+        if cur is not None:
+            lines.append(line)
+            if re.match(r"^\.Lfunc_end\d+:", line):
+                bodies[cur] = hashlib.sha256("\n".join(lines).encode()).hexdigest()
+                cur = None
+    names = sorted(bodies)
+    kernels = dict(zip(_demangle(names), (bodies[n] for n in names)))
+    return hashlib.sha256(text.encode()).hexdigest(), kernels
 
 
 def build(verbose=False, debug=False):
@@ -89,8 +116,10 @@ def build(verbose=False, debug=False):
         hashes = [] if debug else [ex.submit(device_code_sha256, k, verbose) for k in KERNEL_SOURCES]
         list(ex.map(lambda c: _run(c, verbose), cmds))
         if not debug:
-            json.dump({k: h.result() for k, h in zip(KERNEL_SOURCES, hashes)},
-                      open(DEVICE_CODE_PATH, "w"), indent=1)
+            rec = {"kernels": {}}
+            for k, h in zip(KERNEL_SOURCES, hashes):
+                rec[k], rec["kernels"][k] = h.result()
+            json.dump(rec, open(DEVICE_CODE_PATH, "w"), indent=1)
     tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, lib)
