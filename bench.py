@@ -623,6 +623,24 @@ def main():
     _log(f"graph replay: {ms_per_step:.3f} ms per step")
 
     graph_ms = ms_per_step
+    # Spread of the layer-step time: HIP events on the launch stream around
+    # single replays of the step graph (at least 20), each replay's time per
+    # layer-step; median and 10th / 90th percentiles.
+    cur_stream = torch.cuda.current_stream(dev)
+    spread = []
+    for _ in range(max(20, n_replays)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(cur_stream)
+        graphs["step"].replay()
+        e1.record(cur_stream)
+        e1.synchronize()
+        spread.append(e0.elapsed_time(e1) * 1e3 / (reps * n_layers))
+    spread.sort()
+
+    def pct(q):
+        return round(spread[min(len(spread) - 1, int(round(q * (len(spread) - 1))))], 3)
+
     # the headline is the faster of graph replay and eager issue
     timing_mode = "graph" if graph_ms <= eager_ms else "eager"
     ms_per_step = min(graph_ms, eager_ms)
@@ -710,6 +728,7 @@ def main():
         "dtype": "fp8" if fp8 and terms == 2 else "bf16",
         "data": "synthetic",
         "us_per_layer_step": round(us_per_layer, 3),
+        "us_per_layer_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "config": {
             "workload": cfg["desc"],
