@@ -930,6 +930,8 @@ static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 1
 
 // Eight waves in two groups of four; group g owns query rows 32g..32g+31 and
 // waves 4g..4g+3, and SIMD k runs wave k of group 0 and wave k of group 1.
+// (Group 1 of a block of at most 48 rows is packed: its at most 16 rows
+// carry both FP8 terms in one 32-row operand, see pk in the kernel.)
 // Within a group, wave v = w & 3:
 //   QK:  position half sp = v & 1 of the 64-position tile (a 32-position
 //        block) and dimension half dh = v >> 1 (k-steps 0..4 or 5..8 of 64
@@ -1009,6 +1011,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int b = wc.b;
   // rows 64 * wc.z .. + 63 of the Q*H query rows are this workgroup's
   const int myrow = 64 * wc.z + 32 * grp + r32;
+  // Packed group: group 1 of a row block holding at most 48 rows has at most
+  // 16 real rows, so the two FP8 terms of its operands share one 32-row MFMA
+  // operand instead of taking an MFMA each: MFMA row n < 16 carries the first
+  // term of the group's row n, row n + 16 its second term.  Its score
+  // products and its output then come out as two halves, added back per row
+  // (the scores in the softmax, the output in the epilogue), and the group
+  // issues half the MFMAs of an unpacked one.
+  const bool pack = R - 64 * wc.z <= 48;
+  const bool pk = grp == 1 && pack;
 
   // seq_lens[b] is requested first (a scalar load, waited for below), then
   // the query block's loads go out: they need only the workgroup's
@@ -1053,10 +1064,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // copied by both groups while they run their softmax, two tiles ahead:
   // group 1 loads 0..kLoads1-1 of each page at E(T - 2), group 0 the rest at
   // O(T - 2), so the copy issue never sits on the MFMA-role path and is shared
-  // between the two softmax phases.  A page outside the split, or the
+  // between the two softmax phases.  In a packed workgroup (see pk below) the
+  // two group-1 waves with no softmax rows (dh = 1) copy whole pages v4 and
+  // v4 ^ 2 at E(T - 2) and no other wave copies: no softmax wave waits on a
+  // copy issue (c4 split kernel -4%, long context -1.6% against the shared
+  // copies, same-box timing).  A page outside the split, or the
   // positions past seq_len in the last page, lie outside the buffer range and
   // are written to LDS as zeros by the copy itself.
-  // Page-table entry of page v4 of tile T (entries past the sequence are
+  // Page-table entry of page pg (v4 unless given) of tile T (entries past the sequence are
   // clamped to its last page and not used), read through the constant
   // address space: the index is wave-uniform, so this is a scalar load,
   // which does not count against vmcnt.
@@ -1064,18 +1079,19 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const __attribute__((address_space(4))) int32_t* pt_b =
       (const __attribute__((address_space(4))) int32_t*)(a.page_table + (int64_t)b * a.max_blocks);
   const int plast = max(P - 1, 0);
-  auto pt_load = [&](int T) -> int {
-    return pt_b[min(p0 + T * kTilePages + v4, plast)];
+  auto pt_load_pg = [&](int T, int pg) -> int {
+    return pt_b[min(p0 + T * kTilePages + pg, plast)];
   };
-  // loads C0 .. C1 - 1 (compile-time range) of page v4 of tile T
-  auto issue_part = [&](int T, int ptv, auto C0, auto C1) {
+  auto pt_load = [&](int T) -> int { return pt_load_pg(T, v4); };
+  // loads C0 .. C1 - 1 (compile-time range) of page pg of tile T
+  auto issue_page = [&](int T, int pg, int ptv, auto C0, auto C1) {
     constexpr int c0 = decltype(C0)::value, c1 = decltype(C1)::value;
-    const int gp = p0 + T * kTilePages + v4;
+    const int gp = p0 + T * kTilePages + pg;
     int blk = __builtin_amdgcn_readfirstlane(ptv);
     if constexpr (kDebug) blk = gp < p1 ? debug_page_id(blk, a.num_blocks, a.debug_flags) : 0;
     const int bytes = gp < p1 ? min(kPage, L - gp * kPage) * G::kRowB : 0;
     const u32x4 rsrc = buffer_rsrc(a.kv + (int64_t)(gp < p1 ? blk : 0) * G::kPageB, bytes);
-    uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + v4 * G::kPageB;
+    uint8_t* dst = kv_lds + (T % kNBuf) * kTileB + pg * G::kPageB;
     // LDS slot s = 64c + lane of the page holds source chunk
     // 36 row + (x ^ swz(row)) with row = s / 36, x = s % 36.  As 36 is a
     // multiple of 4 the XOR only touches the two low bits, so the source chunk
@@ -1097,6 +1113,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       copy16_to_lds(rsrc, voff, lds_addr(dst + 1024 * c));
     }
   };
+  auto issue_part = [&](int T, int ptv, auto C0, auto C1) { issue_page(T, v4, ptv, C0, C1); };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, kLoads1>;
   using I9 = std::integral_constant<int, kWaveLoads>;
@@ -1121,11 +1138,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // between the reads and the writes.  Waves whose rows are all padding only
   // write zeros.
   i32x8 q1[5], q2[5];
-  int ptA, ptB;   // group 1: page-table entries of the next two tiles to copy
+  int ptA, ptB;   // page-table entries of page v4 of the next two tiles to copy
+  int ptA2, ptB2;  // the same for page v4 ^ 2 (the copying waves of a packed workgroup)
   const int pt0 = pt_load(grp);   // page v4 of the group's first tile
   {
     ptA = pt_load(2);
     ptB = pt_load(3);
+    ptA2 = pt_load_pg(2, v4 ^ 2);
+    ptB2 = pt_load_pg(3, v4 ^ 2);
     // The probability terms and block data read by each group's first PV
     // are zeros (that PV adds nothing; published by the barrier below).
     for (int i = tid; i < (int)(sizeof(p_lds) / 16); i += kF8Threads) ((u32x4*)p_lds)[i] = u32x4{};
@@ -1189,8 +1209,10 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     }
     lds_barrier();   // every row's terms and scale are in place
     {
-      const int lr = 32 * grp + r32;                  // the lane's fragment row
-      const uint8_t* const fb = qlds + lr * (2 * kLatent) + 64 * ks0;
+      // the lane's fragment row (packed: first term of row r32 for lanes of
+      // rows 0..15, second term of row r32 - 16 for the others)
+      const int lr = pk ? 32 + (r32 & 15) : 32 * grp + r32;
+      const uint8_t* const fb = qlds + lr * (2 * kLatent) + 64 * ks0 + (pk && r32 >= 16 ? kLatent : 0);
       const int sw = (lr >> 1) & 3;
       const int o0 = 16 * ((2 * h) ^ sw), o1 = 16 * ((2 * h + 1) ^ sw);
       auto frag = [&](int off) -> i32x8 {
@@ -1201,11 +1223,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         q1[ks] = frag(64 * ks);
-        q2[ks] = frag(64 * ks + kLatent);
+        q2[ks] = pk ? i32x8{} : frag(64 * ks + kLatent);   // (packed: not used)
       }
       // dh = 1 has four k-steps: its fifth query terms are zeros
       q1[4] = dh ? i32x8{} : frag(256);
-      q2[4] = dh ? i32x8{} : frag(256 + kLatent);
+      q2[4] = (dh || pk) ? i32x8{} : frag(256 + kLatent);
     }
   }
   // scale into the log2 domain of the scores this lane handles in the
@@ -1338,6 +1360,19 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
         x[k] = a0[k] + u0[k];
         x[4 + k] = a1[k] + u1[k];
       }
+      if (pk) {
+        // packed group (only its dh = 0 waves run the softmax): set 1 holds
+        // the second query term's products of the same rows, lane for lane
+        const f32x4 b0 = xbuf[w][1][0][ln];
+        const f32x4 b1 = xbuf[w][1][1][ln];
+        const f32x4 t0 = xbuf[w ^ 2][1][0][ln];
+        const f32x4 t1 = xbuf[w ^ 2][1][1][ln];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[k] += b0[k] + t0[k];
+          x[4 + k] += b1[k] + t1[k];
+        }
+      }
     }
     const int tpos0 = (p0 + T * kTilePages) * kPage;
     const int tlim = (p1 - p0 - T * kTilePages) * kPage;
@@ -1432,10 +1467,18 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // group's vector-memory order is its share of tiles 2, 3, 4 ... (group 1:
   // tile 1 whole before them): before E(T), T >= 1, its share of tile T must
   // have landed while that of tile T + 1 may still be in flight.
+  // In a packed workgroup the copying waves (group 1, dh = 1) have tile
+  // T + 1's 18 loads in flight at most, group 1's other waves only their
+  // share of tile 1, and group 0 no copy in the loop.
   auto begin = [&](int hs) {
     if ((hs & 1) == 0 && hs >= 2) {
-      if (grp) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
+      if (grp) {
+        if (!pack) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
+        else if (dh) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kWaveLoads));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      } else if (!pack) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
+      }
     }
     lds_barrier();
   };
@@ -1445,7 +1488,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // would hold the softmax up).  The page-table entries are scalar loads,
   // requested two tiles ahead.
   auto copies = [&](int hs) {
-    if ((hs & 1) == 1 - grp) {
+    if ((hs & 1) == 1 - grp && !pack) {
       const int it = hs >> 1;
       const int cur = (it & 1) ? ptB : ptA;
       const int nxt = pt_load(it + 4);
@@ -1453,6 +1496,23 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       else issue_part(it + 2, cur, I1{}, I9{});
       if (it & 1) ptB = nxt;
       else ptA = nxt;
+    } else if (pack && grp && dh && (hs & 1) == 0) {
+      // packed workgroup: the two group-1 waves without softmax rows copy
+      // whole pages v4 and v4 ^ 2
+      const int it = hs >> 1;
+      const int cur = (it & 1) ? ptB : ptA;
+      const int cur2 = (it & 1) ? ptB2 : ptA2;
+      const int nxt = pt_load(it + 4);
+      const int nxt2 = pt_load_pg(it + 4, v4 ^ 2);
+      issue_page(it + 2, v4, cur, I0{}, I9{});
+      issue_page(it + 2, v4 ^ 2, cur2, I0{}, I9{});
+      if (it & 1) {
+        ptB = nxt;
+        ptB2 = nxt2;
+      } else {
+        ptA = nxt;
+        ptA2 = nxt2;
+      }
     }
   };
   // MFMA role, the phase's critical path (its instructions go first on the
@@ -1468,10 +1528,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // are never used.
   // ---- a6: O^T[c][r] += V^T[c][t] (p1 + p2)^T[t][r], columns 128v .. 128v + 127,
   // with the block's E8M0 scale on operand B.
-  auto mfma_phase = [&](int T) {
+  // Packed (PK): one MFMA per k-step and per column tile, the operand rows
+  // carrying both terms (MFMA row n: row n % 16 of the group, term n / 16);
+  // the block data of MFMA row n are those of row n % 16.
+  auto mfma_phase = [&](int T, auto PKc) {
+    constexpr bool PK = decltype(PKc)::value;
     __builtin_amdgcn_s_setprio(2);
     const int ln = lane_now();
-    const int row = ln & 31;
+    const int row = PK ? (ln & 15) : (ln & 31);
     const f32x4 bk = blk[grp][row];
     const uint8_t* kp = kptr(T);
     const int d1 = kpair();
@@ -1479,66 +1543,70 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     i32x8 kb = kop(kp, d1, 1);
     i32x8 pf[2];
     {
-      const uint8_t* pp = pg_lds + row * kPRB + 16 * (ln >> 5);
+      const uint8_t* pp = pg_lds + row * kPRB + 16 * (ln >> 5) + (PK && (ln & 16) ? kPTerm : 0);
       const u32x4 a0 = *(const u32x4*)pp;
       const u32x4 a1 = *(const u32x4*)(pp + 32);
-      const u32x4 b0 = *(const u32x4*)(pp + kPTerm);
-      const u32x4 b1 = *(const u32x4*)(pp + kPTerm + 32);
       pf[0] = __builtin_bit_cast(i32x8, u32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-      pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
+      if constexpr (!PK) {
+        const u32x4 b0 = *(const u32x4*)(pp + kPTerm);
+        const u32x4 b1 = *(const u32x4*)(pp + kPTerm + 32);
+        pf[1] = __builtin_bit_cast(i32x8, u32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
+      }
     }
+    // one k-step (both query terms unless packed) and one column tile of PV
+    auto qk = [&](const i32x8& k, int ks, f32x16 acc) -> f32x16 {
+      acc = mfma_f8(k, q1[ks], acc);
+      if constexpr (!PK) acc = mfma_f8(k, q2[ks], acc);
+      return acc;
+    };
+    auto pv = [&](int c, int e) {
+      o[c] = mfma_f8s(vfr[c], pf[0], o[c], e);
+      if constexpr (!PK) o[c] = mfma_f8s(vfr[c], pf[1], o[c], e);
+    };
+    constexpr int kT = PK ? 1 : 2;   // MFMAs per k-step and per column tile
     f32x16 s = f32x16{};
-    s = mfma_f8(ka, q1[0], s);
-    s = mfma_f8(ka, q2[0], s);
+    s = qk(ka, 0, s);
     const int e = rebase(bk, s);
     ka = kop(kp, d1, 2);
-    s = mfma_f8(kb, q1[1], s);
-    s = mfma_f8(kb, q2[1], s);
+    s = qk(kb, 1, s);
     kb = kop(kp, d1, 3);
-    s = mfma_f8(ka, q1[2], s);
-    s = mfma_f8(ka, q2[2], s);
+    s = qk(ka, 2, s);
     // the dh = 1 waves have four k-steps: their fifth reuses the fourth's
     // keys against zero query terms (no branch, so the phase is one block;
     // the dh = 0 waves on the other SIMDs run five steps anyway)
     ka = kop(kp, d1, dh ? 3 : 4);
-    s = mfma_f8(kb, q1[3], s);
-    s = mfma_f8(kb, q2[3], s);
-    s = mfma_f8(ka, q1[4], s);
-    s = mfma_f8(ka, q2[4], s);
+    s = qk(kb, 3, s);
+    s = qk(ka, 4, s);
     const uint8_t* vp = kv_lds + (T % kNBuf) * kTileB + vbase_now();
     // written out: a rolled loop here makes the compiler rotate the four
     // accumulators through one register window with moves
-    o[0] = mfma_f8s(vfr[0], pf[0], o[0], e);
-    o[0] = mfma_f8s(vfr[0], pf[1], o[0], e);
+    pv(0, e);
     vfr[0] = vread(vp, 0);
-    o[1] = mfma_f8s(vfr[1], pf[0], o[1], e);
-    o[1] = mfma_f8s(vfr[1], pf[1], o[1], e);
+    pv(1, e);
     vfr[1] = vread(vp, 1);
     send_scores(s);
-    o[2] = mfma_f8s(vfr[2], pf[0], o[2], e);
-    o[2] = mfma_f8s(vfr[2], pf[1], o[2], e);
+    pv(2, e);
     vfr[2] = vread(vp, 2);
-    o[3] = mfma_f8s(vfr[3], pf[0], o[3], e);
-    o[3] = mfma_f8s(vfr[3], pf[1], o[3], e);
+    pv(3, e);
     vfr[3] = vread(vp, 3);
     // Order after the rescale check: each k-step's key reads two MFMAs ahead
     // of their use, then the PV pairs with each column tile's value reads after it
     // and the score exchange's LDS writes in the middle.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // keys, step 2
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // QK, step 1
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // keys, step 3
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // QK, step 2
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // keys, step 4
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // QK, steps 3 and 4
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV, column tile 0
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 0
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV 1
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 1
-    __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);   // scores to LDS
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV 2
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 2
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // PV 3
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // values 3
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // keys, step 2
+    __builtin_amdgcn_sched_group_barrier(0x008, kT, 0);       // QK, step 1
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // keys, step 3
+    __builtin_amdgcn_sched_group_barrier(0x008, kT, 0);       // QK, step 2
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // keys, step 4
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kT, 0);   // QK, steps 3 and 4
+    __builtin_amdgcn_sched_group_barrier(0x008, kT, 0);       // PV, column tile 0
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // values 0
+    __builtin_amdgcn_sched_group_barrier(0x008, kT, 0);       // PV 1
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // values 1
+    __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);        // scores to LDS
+    __builtin_amdgcn_sched_group_barrier(0x008, kT, 0);       // PV 2
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // values 2
+    __builtin_amdgcn_sched_group_barrier(0x008, kT, 0);       // PV 3
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // values 3
     __builtin_amdgcn_s_setprio(0);
   };
   if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -1546,17 +1614,23 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // when Q*H is an odd multiple of 32) does no matrix or softmax work: its
   // waves only take part in the barriers and issue their share of the copies.
   const bool live = 64 * wc.z + 32 * grp < R;
-  for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
-    begin(hs);
-    const int st = hs - grp;
-    if (live && st >= 0 && (st & 1) == 0) {
-      mfma_phase(st >> 1);
-    } else if (live && st >= 1) {
-      const int T = (st - 1) >> 1;
-      if (T < ntiles) softmax(T);
+  // The packed and unpacked groups run separate copies of the loop (one
+  // loop holding both MFMA phases would need more registers than a wave has).
+  auto run = [&](auto PKc) {
+    for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
+      begin(hs);
+      const int st = hs - grp;
+      if (live && st >= 0 && (st & 1) == 0) {
+        mfma_phase(st >> 1, PKc);
+      } else if (live && st >= 1 && !(decltype(PKc)::value && dh)) {   // (packed: dh = 1 has no rows)
+        const int T = (st - 1) >> 1;
+        if (T < ntiles) softmax(T);
+      }
+      copies(hs);
     }
-    copies(hs);
-  }
+  };
+  if (pk) run(std::true_type{});
+  else run(std::false_type{});
 
   // No copy may still be writing this workgroup's LDS when it ends, and the
   // epilogue reuses the KV buffers: every wave's copies have landed.
@@ -1572,6 +1646,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
     static_assert(kF8Waves * 32 * kSRow <= kNBuf * kTileB, "epilogue staging fits the KV buffers");
     uint8_t* const stage = kv_lds + w * 32 * kSRow;
     const float sc = l_run > 0.f ? a.out_scale / l_run : 0.f;
+    if (pk) {
+      // packed: output row n % 16 is the sum of MFMA rows n and n ^ 16 (the
+      // two probability terms), held by lanes l and l ^ 16; both lanes of a
+      // pair add in the same order, and only rows 0..15 are stored
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) o[ct][k] = sum16(o[ct][k]);
+    }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
