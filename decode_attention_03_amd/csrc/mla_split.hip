@@ -2004,12 +2004,19 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_b16x64(SplitArgs a
   // a group whose 32 rows all lie past Q*H only takes part in the barriers
   // and the copies
   const bool live = 64 * wc.z + 32 * grp < R;
+  // A wave whose eight softmax rows all lie past Q*H skips the softmax (the
+  // probabilities of those rows stay zero and their rescale factors one, as
+  // set in the prologue; rows that are never stored).  Bf16 verify B=32 (36
+  // rows, group 1's waves 1..3): layer-step 173.5 -> 170.0 us, same-box
+  // timing.  Handing those waves the copies as well was slower (180-185 us):
+  // this kernel's copies want the raised priority of the softmax role.
+  const bool srows = 64 * wc.z + 32 * grp + 8 * v4 < R;
   for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
     begin(hs);
     const int st = hs - grp;
     if (live && st >= 0 && (st & 1) == 0) {
       mfma_phase(st >> 1);
-    } else if (live && st >= 1) {
+    } else if (srows && st >= 1) {
       const int T = (st - 1) >> 1;
       if (T < ntiles) softmax(T);
     }
