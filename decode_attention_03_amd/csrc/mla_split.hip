@@ -969,7 +969,7 @@ static_assert(pv_voff(2, 0) == 64 && pv_voff(2, 1) == 4704 && pv_voff(2, 2) == 1
 // reference m only sets the exponent range of the fp32 accumulators: it
 // moves (by an exact power of two applied to O and l) when a tile maximum
 // passes it by more than 2^kSlack, and nothing is ever recomputed.
-template <bool FINAL>
+template <bool FINAL, bool PACK>
 __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using G = KvGeom<true>;
@@ -1011,15 +1011,19 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   const int b = wc.b;
   // rows 64 * wc.z .. + 63 of the Q*H query rows are this workgroup's
   const int myrow = 64 * wc.z + 32 * grp + r32;
-  // Packed group: group 1 of a row block holding at most 48 rows has at most
-  // 16 real rows, so the two FP8 terms of its operands share one 32-row MFMA
-  // operand instead of taking an MFMA each: MFMA row n < 16 carries the first
-  // term of the group's row n, row n + 16 its second term.  Its score
-  // products and its output then come out as two halves, added back per row
-  // (the scores in the softmax, the output in the epilogue), and the group
-  // issues half the MFMAs of an unpacked one.
-  const bool pack = R - 64 * wc.z <= 48;
-  const bool pk = grp == 1 && pack;
+  // Packed group (PACK: launched for 33..48 query rows, one row block):
+  // group 1 then has at most 16 real rows, so the two FP8 terms of its
+  // operands share one 32-row MFMA operand instead of taking an MFMA each:
+  // MFMA row n < 16 carries the first term of the group's row n, row n + 16
+  // its second term.  Its score products and its output then come out as two
+  // halves, added back per row (the scores in the softmax, the output in the
+  // epilogue), and the group issues half the MFMAs of an unpacked one.  The
+  // copies are placed differently too (cpk, below).  Other row counts run
+  // the kernel without any of it: carrying the packed code, the unpacked
+  // blocks of the DCP8 shape ran 2.4% slower (more scalar registers, a
+  // longer kernel).
+  const bool pk = PACK && grp == 1;
+  const bool cpk = PACK;
 
   // seq_lens[b] is requested first (a scalar load, waited for below), then
   // the query block's loads go out: they need only the workgroup's
@@ -1139,13 +1143,10 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // write zeros.
   i32x8 q1[5], q2[5];
   int ptA, ptB;   // page-table entries of page v4 of the next two tiles to copy
-  int ptA2, ptB2;  // the same for page v4 ^ 2 (the copying waves of a packed workgroup)
   const int pt0 = pt_load(grp);   // page v4 of the group's first tile
   {
     ptA = pt_load(2);
     ptB = pt_load(3);
-    ptA2 = pt_load_pg(2, v4 ^ 2);
-    ptB2 = pt_load_pg(3, v4 ^ 2);
     // The probability terms and block data read by each group's first PV
     // are zeros (that PV adds nothing; published by the barrier below).
     for (int i = tid; i < (int)(sizeof(p_lds) / 16); i += kF8Threads) ((u32x4*)p_lds)[i] = u32x4{};
@@ -1470,14 +1471,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // In a packed workgroup the copying waves (group 1, dh = 1) have tile
   // T + 1's 18 loads in flight at most, group 1's other waves only their
   // share of tile 1, and group 0 no copy in the loop.
-  auto begin = [&](int hs) {
+  auto begin = [&](int hs, auto PKc) {
     if ((hs & 1) == 0 && hs >= 2) {
-      if (grp) {
-        if (!pack) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
+      if constexpr (decltype(PKc)::value) {   // group 1, packed
+        if (!cpk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
         else if (dh) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kWaveLoads));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      } else if (!pack) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
+      } else {
+        if (grp) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
+        else if (!cpk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
       }
     }
     lds_barrier();
@@ -1486,33 +1488,34 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // softmax phases), group 0 at odd ones (its softmax phases), after the
   // softmax work (issued first, a copy that stalls on a full memory queue
   // would hold the softmax up).  The page-table entries are scalar loads,
-  // requested two tiles ahead.
-  auto copies = [&](int hs) {
-    if ((hs & 1) == 1 - grp && !pack) {
-      const int it = hs >> 1;
-      const int cur = (it & 1) ? ptB : ptA;
+  // requested two tiles ahead (the copying waves of a packed workgroup read
+  // their second page's entry when they issue: they have no other work then).
+  auto copies = [&](int hs, auto PKc) {
+    const int it = hs >> 1;
+    auto next_entries = [&](int cur) {
       const int nxt = pt_load(it + 4);
-      if (grp) issue_part(it + 2, cur, I0{}, I1{});
-      else issue_part(it + 2, cur, I1{}, I9{});
       if (it & 1) ptB = nxt;
       else ptA = nxt;
-    } else if (pack && grp && dh && (hs & 1) == 0) {
-      // packed workgroup: the two group-1 waves without softmax rows copy
-      // whole pages v4 and v4 ^ 2
-      const int it = hs >> 1;
-      const int cur = (it & 1) ? ptB : ptA;
-      const int cur2 = (it & 1) ? ptB2 : ptA2;
-      const int nxt = pt_load(it + 4);
-      const int nxt2 = pt_load_pg(it + 4, v4 ^ 2);
-      issue_page(it + 2, v4, cur, I0{}, I9{});
-      issue_page(it + 2, v4 ^ 2, cur2, I0{}, I9{});
-      if (it & 1) {
-        ptB = nxt;
-        ptB2 = nxt2;
-      } else {
-        ptA = nxt;
-        ptA2 = nxt2;
+      (void)cur;
+    };
+    if constexpr (decltype(PKc)::value) {   // group 1, packed
+      if ((hs & 1) == 0) {
+        const int cur = (it & 1) ? ptB : ptA;
+        if (!cpk) {
+          issue_part(it + 2, cur, I0{}, I1{});
+          next_entries(cur);
+        } else if (dh) {
+          const int cur2 = pt_load_pg(it + 2, v4 ^ 2);
+          issue_page(it + 2, v4, cur, I0{}, I9{});
+          issue_page(it + 2, v4 ^ 2, cur2, I0{}, I9{});
+          next_entries(cur);
+        }
       }
+    } else if ((hs & 1) == 1 - grp && !(cpk && grp == 0)) {
+      const int cur = (it & 1) ? ptB : ptA;
+      if (grp) issue_part(it + 2, cur, I0{}, I1{});
+      else issue_part(it + 2, cur, I1{}, I9{});
+      next_entries(cur);
     }
   };
   // MFMA role, the phase's critical path (its instructions go first on the
@@ -1618,7 +1621,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // loop holding both MFMA phases would need more registers than a wave has).
   auto run = [&](auto PKc) {
     for (int hs = 0; hs <= 2 * ntiles + 1; ++hs) {
-      begin(hs);
+      begin(hs, PKc);
       const int st = hs - grp;
       if (live && st >= 0 && (st & 1) == 0) {
         mfma_phase(st >> 1, PKc);
@@ -1626,11 +1629,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
         const int T = (st - 1) >> 1;
         if (T < ntiles) softmax(T);
       }
-      copies(hs);
+      copies(hs, PKc);
     }
   };
-  if (pk) run(std::true_type{});
-  else run(std::false_type{});
+  if constexpr (PACK) {
+    if (pk) run(std::true_type{});
+    else run(std::false_type{});
+  } else {
+    run(std::false_type{});
+  }
 
   // No copy may still be writing this workgroup's LDS when it ends, and the
   // epilogue reuses the KV buffers: every wave's copies have landed.
@@ -2090,10 +2097,17 @@ hipError_t launch_dtype(const SplitArgs& a, bool final_out, hipStream_t stream) 
   if (rows > 32) {
     const dim3 grid((unsigned)(a.num_splits * a.batch * ((rows + 63) / 64)));
     if constexpr (FP8) {
-      if (final_out)
-        hipLaunchKernelGGL(split_kernel_f8x64<true>, grid, dim3(kF8Threads), 0, stream, a);
-      else
-        hipLaunchKernelGGL(split_kernel_f8x64<false>, grid, dim3(kF8Threads), 0, stream, a);
+      if (rows <= 48) {   // one row block whose group 1 is packed
+        if (final_out)
+          hipLaunchKernelGGL((split_kernel_f8x64<true, true>), grid, dim3(kF8Threads), 0, stream, a);
+        else
+          hipLaunchKernelGGL((split_kernel_f8x64<false, true>), grid, dim3(kF8Threads), 0, stream, a);
+      } else {
+        if (final_out)
+          hipLaunchKernelGGL((split_kernel_f8x64<true, false>), grid, dim3(kF8Threads), 0, stream, a);
+        else
+          hipLaunchKernelGGL((split_kernel_f8x64<false, false>), grid, dim3(kF8Threads), 0, stream, a);
+      }
     } else {
       if (final_out)
         hipLaunchKernelGGL(split_kernel_b16x64<true>, grid, dim3(kF8Threads), 0, stream, a);
