@@ -71,7 +71,9 @@ def _demangle(names):
 def device_code_sha256(src, verbose=False):
     """sha256 of the gfx950 assembly hipcc emits for one kernel source, with the
     per-compilation unit id symbol (the only part that changes from one
-    compile of the same source to the next) normalised, and the sha256 of
+    compile of the same source to the next) and the function index in local
+    labels and comments (which another kernel added to or removed from the
+    source shifts) normalised, and the sha256 of
     each kernel function's own assembly (label to end of function) by
     demangled name.  Host-only edits of a source leave them unchanged; a
     change of a kernel's device code changes its hash and the file's, and
@@ -81,6 +83,11 @@ def device_code_sha256(src, verbose=False):
         _run([HIPCC] + FLAGS + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out], verbose)
         text = open(out).read()
     text = re.sub(r"__hip_cuid_[0-9a-f]+", "__hip_cuid", text)
+    # local labels carry the function's index in the file (.LBB<f>_<n>,
+    # .Lfunc_end<f>), as do the compiler's comments: adding or removing
+    # another kernel renumbers them.  Comments and trailing blanks go.
+    text = re.sub(r"\.L(BB|func_end|tmp)\d+", r".L\1", text)
+    text = "\n".join(l for l in (re.sub(r"\s*;.*$", "", l).rstrip() for l in text.splitlines()) if l)
     bodies = {}
     cur, lines = None, []
     for line in text.splitlines():
@@ -89,7 +96,7 @@ def device_code_sha256(src, verbose=False):
             cur, lines = m.group(1), []
         if cur is not None:
             lines.append(line)
-            if re.match(r"^\.Lfunc_end\d+:", line):
+            if re.match(r"^\.Lfunc_end\d*:", line):
                 bodies[cur] = hashlib.sha256("\n".join(lines).encode()).hexdigest()
                 cur = None
     names = sorted(bodies)
