@@ -680,8 +680,12 @@ def main():
     rblock = 64 if rows > 32 else 16 if rows <= 16 else 48
     exec_rows = rblock * -(-rows // rblock)
     terms = 2 if (fp8 and rows > 32) else 1
+    # the FP8 kernel packs the second 32-row group of a 33..48-row block: both
+    # terms share one 32-row operand, so that group executes one term's work
+    packed = fp8 and 32 < rows <= 48
+    row_terms = exec_rows * terms - (32 if packed else 0)
     positions = sum(int(l.seq_lens.sum().item()) for l in layers) / n_layers
-    mfma_exec = positions * exec_rows * terms * 2 * (576 + 512)
+    mfma_exec = positions * row_terms * 2 * (576 + 512)
     mfma_peak = 5000.0 if terms == 2 else 2500.0
     # The split kernel is bound by HBM below the MFMA ridge (peak flops / 8 TB/s)
     # and by the matrix cores above it (many heads, e.g. 96 heads at Q = 3).
@@ -763,8 +767,9 @@ def main():
             "peak": mfma_peak,
             "unit": "TFLOP/s",
             "frac": round(mfma_exec / (split_us * 1e-6) / 1e12 / mfma_peak, 4),
-            "note": f"executed = {exec_rows} padded rows x {terms} operand term(s) x "
-                    "2 x (576 + 512) flops per position",
+            "note": f"executed = {exec_rows} padded rows x {terms} operand term(s)"
+                    + (" (the second 32-row group packed: one term's work)" if packed else "")
+                    + " x 2 x (576 + 512) flops per position",
         },
     }
     if joint:
