@@ -87,7 +87,10 @@ def test_wide_row_blocks(gpu_lib, case):
 
 # FP8 blocks of 33..48 query rows: the eight-wave kernel's second wave group
 # holds 1..16 real rows and the rest padding, at both ends of that range and
-# with every causal token count.
+# with every causal token count.  These launch the packed kernel (the group's
+# two FP8 terms in one 32-row operand, its copies issued by its two waves
+# without softmax rows); 49 rows is the first count past it (unpacked, a
+# second row block holding one row).
 PARTIAL_GROUP_CASES = [
     # (seq_lens, Q, H, kv_dtype, num_splits)
     ([3, 63, 64, 65, 129, 300], 3, 16, "fp8", 0),   # 48 rows
@@ -95,6 +98,8 @@ PARTIAL_GROUP_CASES = [
     ([2000, 8], 8, 5, "fp8", 0),                    # 40 rows, eight causal tokens (the
                                                     # first sees one position)
     ([4, 16, 100], 4, 12, "fp8", 1),                # 48 rows, direct bf16 output
+    ([1300, 250], 1, 48, "fp8", 5),                 # 48 rows of one token
+    ([500, 1200], 7, 7, "fp8", 0),                  # 49 rows: unpacked
 ]
 
 
