@@ -1018,12 +1018,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // its second term.  Its score products and its output then come out as two
   // halves, added back per row (the scores in the softmax, the output in the
   // epilogue), and the group issues half the MFMAs of an unpacked one.  The
-  // copies are placed differently too (cpk, below).  Other row counts run
+  // copies are placed differently too (see copies below).  Other row counts run
   // the kernel without any of it: carrying the packed code, the unpacked
   // blocks of the DCP8 shape ran 2.4% slower (more scalar registers, a
   // longer kernel).
   const bool pk = PACK && grp == 1;
-  const bool cpk = PACK;
 
   // seq_lens[b] is requested first (a scalar load, waited for below), then
   // the query block's loads go out: they need only the workgroup's
@@ -1474,12 +1473,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   auto begin = [&](int hs, auto PKc) {
     if ((hs & 1) == 0 && hs >= 2) {
       if constexpr (decltype(PKc)::value) {   // group 1, packed
-        if (!cpk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
-        else if (dh) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kWaveLoads));
+        if (dh) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kWaveLoads));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      } else {
-        if (grp) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
-        else if (!cpk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
+      } else if (grp) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads1));
+      } else if constexpr (!PACK) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWaveLoads - kLoads1));
       }
     }
     lds_barrier();
@@ -1492,30 +1491,24 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
   // their second page's entry when they issue: they have no other work then).
   auto copies = [&](int hs, auto PKc) {
     const int it = hs >> 1;
-    auto next_entries = [&](int cur) {
+    auto next_entries = [&]() {
       const int nxt = pt_load(it + 4);
       if (it & 1) ptB = nxt;
       else ptA = nxt;
-      (void)cur;
     };
-    if constexpr (decltype(PKc)::value) {   // group 1, packed
-      if ((hs & 1) == 0) {
+    if constexpr (decltype(PKc)::value) {   // group 1, packed: its dh = 1 waves copy everything
+      if ((hs & 1) == 0 && dh) {
         const int cur = (it & 1) ? ptB : ptA;
-        if (!cpk) {
-          issue_part(it + 2, cur, I0{}, I1{});
-          next_entries(cur);
-        } else if (dh) {
-          const int cur2 = pt_load_pg(it + 2, v4 ^ 2);
-          issue_page(it + 2, v4, cur, I0{}, I9{});
-          issue_page(it + 2, v4 ^ 2, cur2, I0{}, I9{});
-          next_entries(cur);
-        }
+        const int cur2 = pt_load_pg(it + 2, v4 ^ 2);
+        issue_page(it + 2, v4, cur, I0{}, I9{});
+        issue_page(it + 2, v4 ^ 2, cur2, I0{}, I9{});
+        next_entries();
       }
-    } else if ((hs & 1) == 1 - grp && !(cpk && grp == 0)) {
+    } else if ((hs & 1) == 1 - grp && !(PACK && grp == 0)) {
       const int cur = (it & 1) ? ptB : ptA;
       if (grp) issue_part(it + 2, cur, I0{}, I1{});
       else issue_part(it + 2, cur, I1{}, I9{});
-      next_entries(cur);
+      next_entries();
     }
   };
   // MFMA role, the phase's critical path (its instructions go first on the
