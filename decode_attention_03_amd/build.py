@@ -82,6 +82,16 @@ def device_code_sha256(src, verbose=False):
         out = os.path.join(tmp, "dev.s")
         _run([HIPCC] + FLAGS + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out], verbose)
         text = open(out).read()
+    whole, bodies = assembly_sha256(text)
+    names = sorted(bodies)
+    return whole, dict(zip(_demangle(names), (bodies[n] for n in names)))
+
+
+def assembly_sha256(text):
+    """(sha256 of the whole normalised assembly, {mangled kernel name: sha256
+    of that function's normalised assembly}) for hipcc's assembly `text`: the
+    compile-unit id symbol, the function index in local labels and the
+    compiler's comments are normalised away (see device_code_sha256)."""
     text = re.sub(r"__hip_cuid_[0-9a-f]+", "__hip_cuid", text)
     # local labels carry the function's index in the file (.LBB<f>_<n>,
     # .Lfunc_end<f>), as do the compiler's comments: adding or removing
@@ -99,9 +109,7 @@ def device_code_sha256(src, verbose=False):
             if re.match(r"^\.Lfunc_end\d*:", line):
                 bodies[cur] = hashlib.sha256("\n".join(lines).encode()).hexdigest()
                 cur = None
-    names = sorted(bodies)
-    kernels = dict(zip(_demangle(names), (bodies[n] for n in names)))
-    return hashlib.sha256(text.encode()).hexdigest(), kernels
+    return hashlib.sha256(text.encode()).hexdigest(), bodies
 
 
 def build(verbose=False, debug=False):
