@@ -164,8 +164,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 
 // Shape by the split count of a row.  With the plan by length the rows of the
 // longest sequences, which set the time, hold about twice the average: up to
-// 16 on average that moves the shape to two lanes per chunk (c2, 8 splits:
-// 5.7 -> 5.1 us); at 32 the whole-row shape stays the faster one (c3: 11.9 us
+// 16 on average that moves the shape to two lanes per chunk (bf16 decode of
+// 32 sequences of 1,024..8,192 positions, 8 splits:
+// 5.7 -> 5.1 us); at 32 the whole-row shape stays the faster one (bf16 verify
+// of 32 sequences, 4,096..32,768 positions: 11.9 us
 // against 14.2 for quarter rows).
 int shape_splits(const MergeArgs& a) {
   return (a.by_length && a.num_splits <= 16) ? 2 * a.num_splits : a.num_splits;
