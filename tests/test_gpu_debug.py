@@ -46,9 +46,10 @@ def _run(lib, inp, num_splits):
     return out, lse
 
 
-# (kv dtype, query tokens, heads): the FP8 kernel above 32 rows, the generic
-# kernel with FP8 and with bf16 KV
-SHAPES = [("fp8", 3, 12), ("fp8", 1, 12), ("bf16", 3, 12)]
+# (kv dtype, query tokens, heads): the FP8 eight-wave kernel packed (36 rows)
+# and unpacked (80 rows, two row blocks), the generic kernel with FP8 and with
+# bf16 KV (12 rows), the bf16 eight-wave kernel (36 rows)
+SHAPES = [("fp8", 3, 12), ("fp8", 5, 16), ("fp8", 1, 12), ("bf16", 1, 12), ("bf16", 3, 12)]
 
 
 @pytest.mark.parametrize("dtype,Q,H", SHAPES)
