@@ -1674,7 +1674,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       const int r = 4 * j + (lane >> 4);
       const int grow = 64 * wc.z + 32 * grp + r;
       const u32x4 v = *(const u32x4*)(stage + r * kSRow + 2 * cc);
-      if (grow < R) *(u32x4*)(dst + (row0 + grow) * kValue + 128 * v4 + cc) = v;
+      if (grow < R) {
+        u32x4* const gp = (u32x4*)(dst + (row0 + grow) * kValue + 128 * v4 + cc);
+        // partials of the packed form go out non-temporally: the merge reads
+        // each once, from other XCDs (long context, 4 x 35,500 positions:
+        // layer-step -1.1%, same box; the DCP8 shape's 75 MB of partials ran
+        // slower so, and its unpacked form stores them as usual)
+        if constexpr (PACK && !FINAL) __builtin_nontemporal_store(v, gp);
+        else *gp = v;
+      }
     }
   }
   if (myrow < R && v4 == 0 && h == 0) {
