@@ -160,6 +160,25 @@ __device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t voffset, uint
       : "=&s"(saved)
       : "v"(voffset), "s"(rsrc), "s"(lds_addr));
 }
+// The same with the non-temporal bit, for pages that one launch reads
+// exactly once (a single row block per split): the page stream then does
+// not push out of the L2 what is shared between workgroups (the query rows
+// of a sequence).  Same-box timing: bf16 decode of 32 sequences (generic
+// kernel) 41.9 -> 38.2 us per layer-step, bf16 verify of 32 sequences
+// (eight-wave kernel, one row block) 169.9 -> 167.2 us, packed FP8 kernel:
+// long-context split kernel -1.3%, FP8 verify of 64 sequences -1%.  Kernels
+// whose row blocks share pages (several per split) keep cached loads.
+__device__ __forceinline__ void copy16_to_lds_nt(u32x4 rsrc, uint32_t voffset, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(rsrc), "s"(lds_addr));
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, p);
 }
@@ -448,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         const uint32_t slot = wslot0 + 64 * c + lane;
         const uint32_t row = slot / G::kChunksPerRow;
         const uint32_t x = (slot - row * G::kChunksPerRow) ^ G::swz(row);
-        copy16_to_lds(rsrc, row * G::kRowB + x * 16, lds_addr(dst + 1024 * c));
+        copy16_to_lds_nt(rsrc, row * G::kRowB + x * 16, lds_addr(dst + 1024 * c));
       }
     } else {
 #pragma unroll
@@ -1114,7 +1133,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_f8x64(SplitArgs a)
       const int t = kRowsPerSwz * (d0 + 1) - 64 * c;
       const uint32_t d = (uint32_t)d0 + ((t < 64 && ln >= t) ? 1u : 0u);
       const uint32_t voff = (vb + 1024u * (uint32_t)c) ^ (d << 4);
-      copy16_to_lds(rsrc, voff, lds_addr(dst + 1024 * c));
+      if constexpr (PACK) copy16_to_lds_nt(rsrc, voff, lds_addr(dst + 1024 * c));
+      else copy16_to_lds(rsrc, voff, lds_addr(dst + 1024 * c));
     }
   };
   auto issue_part = [&](int T, int ptv, auto C0, auto C1) { issue_page(T, v4, ptv, C0, C1); };
@@ -1824,7 +1844,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void split_kernel_b16x64(SplitArgs a
       const int t = 144 * (d0 + 1) - base;
       const uint32_t d = (uint32_t)d0 + ((t < 64 && ln >= t) ? 1u : 0u);
       const uint32_t voff = (vb + 16u * (uint32_t)base) ^ (d << 4);
-      copy16_to_lds(rsrc, voff, lds_addr(dst + 16 * base));
+      if (R <= 64) copy16_to_lds_nt(rsrc, voff, lds_addr(dst + 16 * base));
+      else copy16_to_lds(rsrc, voff, lds_addr(dst + 16 * base));
     }
   };
   using I0 = std::integral_constant<int, 0>;
