@@ -101,10 +101,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   // S - 1, row 0 for a dead slice: the buffer holds all of those partials), so
   // no branch with its own wait sits between them; a split past S, like an
   // empty one, has weight zero below and its value is not used.
+  // The partial loads are non-temporal: each partial is read once, and
+  // kept out of the L2 it leaves room for the next launch's stream
+  // (long-context layer-step -2.5%, same box; timed alone, with the same
+  // partials re-read launch after launch, this kernel looks slower so).
   u32x2 v[kInFlight];   // four bf16 each
 #pragma unroll
   for (int u = 0; u < kInFlight; ++u)
-    v[u] = *(const u32x2*)(po + (int64_t)min(lane_s + LANES * u, S - 1) * stride);
+    v[u] = __builtin_nontemporal_load((const u32x2*)(po + (int64_t)min(lane_s + LANES * u, S - 1) * stride));
 
   // (selected only here, after the partial loads have been issued)
   const float ls0 = (live && t < S) ? ls_t : kNegInf;
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       if (s0 != lane_s) {   // later rounds (S > LANES * kInFlight)
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u)
-          v[u] = *(const u32x2*)(po + (int64_t)min(s0 + LANES * u, S - 1) * stride);
+          v[u] = __builtin_nontemporal_load((const u32x2*)(po + (int64_t)min(s0 + LANES * u, S - 1) * stride));
       }
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u) {
